@@ -1,0 +1,186 @@
+"""CPU oracle for the DiT flash self-attention path.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product library never imports,
+links or loads anything from this package, and this package never imports the
+product library.
+
+The arithmetic lives in oracle.c (plain C, fp64 attention, IEEE fp32
+quantizer); this module only marshals numpy arrays through ctypes.  Inputs are
+BF16 bit patterns as numpy uint16 arrays in [B, S, H, D] order.
+
+Citations (page title, section):
+  * exact attention: "Kernel acceleration: attention, compilation and fusion",
+    section "Attention: from O(N^2) memory to blocks" (naive and blocked forms);
+  * quantizer: "gfx1201_sage_prepare / gfx1201_sage_attention" (aiter PR 6390),
+    section "Technical Details" (INT8 Q/K with one FP32 scale per 32-row block,
+    Q carrying softmax_scale * log2(e); FP8 e4m3 V with one scale per channel,
+    transposed to [B, H, 128, S_pad]).
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+LOG2E = 1.4426950408889634
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.build(force=False)
+        lib = ctypes.CDLL(path)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i8p = ctypes.POINTER(ctypes.c_int8)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        ci, cf = ctypes.c_int, ctypes.c_float
+        lib.oracle_num_threads.restype = ci
+        lib.oracle_softmax_row.argtypes = [u16p, u16p, ci, ci, ci, ci, cf, ci, ci, ci, f64p]
+        lib.oracle_attn_rows.argtypes = [u16p, u16p, u16p, ci, ci, ci, ci, cf, i64p,
+                                         ctypes.c_int64, f64p, ci]
+        lib.oracle_attn_blocked.argtypes = [u16p, u16p, u16p, ci, ci, ci, ci, cf, ci, ci, f64p]
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [cf]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_sage_padded_len.argtypes = [ci]
+        lib.oracle_sage_padded_len.restype = ci
+        lib.oracle_quant_qk.argtypes = [u16p, ci, ci, ci, ci, cf, ci, i8p, f32p]
+        lib.oracle_quant_v.argtypes = [u16p, ci, ci, ci, ci, ci, u8p, f32p]
+        for name in ("oracle_softmax_row", "oracle_attn_rows", "oracle_attn_blocked",
+                     "oracle_quant_qk", "oracle_quant_v"):
+            getattr(lib, name).restype = ci
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _bits(x):
+    """Accept a BF16 bit array (uint16/int16) or a torch bfloat16 tensor."""
+    if hasattr(x, "dtype") and str(x.dtype) == "torch.bfloat16":
+        import torch
+        x = x.detach().cpu().contiguous().view(torch.int16).numpy()
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.int16:
+        x = x.view(np.uint16)
+    if x.dtype != np.uint16:
+        raise TypeError("expected BF16 bit patterns (uint16), got %s" % x.dtype)
+    return x
+
+
+def _check(status, what):
+    if status != 0:
+        raise RuntimeError("%s failed with oracle status %d" % (what, status))
+
+
+def num_threads():
+    return _lib().oracle_num_threads()
+
+
+def q_multiplier(scale):
+    """c = float32(double(scale) * log2(e)): the factor Q carries into INT8."""
+    return float(np.float32(float(np.float32(scale)) * LOG2E))
+
+
+def softmax_row(q, k, scale, b, h, i):
+    """Probabilities p_j of query row (b, h, i) over all S keys (fp64)."""
+    q, k = _bits(q), _bits(k)
+    B, S, H, D = q.shape
+    p = np.empty(S, dtype=np.float64)
+    _check(_lib().oracle_softmax_row(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                     B, S, H, D, scale, b, h, i, _ptr(p, ctypes.c_double)),
+           "oracle_softmax_row")
+    return p
+
+
+def attn_rows(q, k, v, scale, rows=None, nthreads=0):
+    """Exact fp64 attention for the query rows `rows` (n x 3 array of b, h, i).
+
+    rows=None means every row; the result then has shape [B, S, H, D], else
+    [n, D].
+    """
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, S, H, D = q.shape
+    full = rows is None
+    if full:
+        b, i, h = np.meshgrid(np.arange(B), np.arange(S), np.arange(H), indexing="ij")
+        rows = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], D), dtype=np.float64)
+    _check(_lib().oracle_attn_rows(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                   _ptr(v, ctypes.c_uint16), B, S, H, D, scale,
+                                   _ptr(rows, ctypes.c_int64), rows.shape[0],
+                                   _ptr(out, ctypes.c_double), nthreads),
+           "oracle_attn_rows")
+    if full:
+        return out.reshape(B, S, H, D)
+    return out
+
+
+def attn_blocked(q, k, v, scale, bq=64, bk=64):
+    """Blocked online-softmax attention over every row, fp64, [B, S, H, D]."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, S, H, D = q.shape
+    out = np.empty((B, S, H, D), dtype=np.float64)
+    _check(_lib().oracle_attn_blocked(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                      _ptr(v, ctypes.c_uint16), B, S, H, D, scale, bq, bk,
+                                      _ptr(out, ctypes.c_double)),
+           "oracle_attn_blocked")
+    return out
+
+
+def e4m3_decode(code):
+    return _lib().oracle_e4m3_decode(int(code) & 0xFF)
+
+
+def e4m3_encode(x):
+    return int(_lib().oracle_e4m3_encode(float(x)))
+
+
+def sage_padded_len(S):
+    return int(_lib().oracle_sage_padded_len(int(S)))
+
+
+def quant_qk(x, mult):
+    """INT8 block quantization: codes [B, H, S_pad, D] int8, scales [B, H, S_pad/32] fp32."""
+    x = _bits(x)
+    B, S, H, D = x.shape
+    S_pad = sage_padded_len(S)
+    codes = np.empty((B, H, S_pad, D), dtype=np.int8)
+    scales = np.empty((B, H, S_pad // 32), dtype=np.float32)
+    _check(_lib().oracle_quant_qk(_ptr(x, ctypes.c_uint16), B, S, H, D, float(mult), S_pad,
+                                  _ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_float)),
+           "oracle_quant_qk")
+    return codes, scales
+
+
+def quant_v(v):
+    """FP8 e4m3 per-channel quantization, transposed: codes [B, H, D, S_pad] uint8, scales [B, H, D]."""
+    v = _bits(v)
+    B, S, H, D = v.shape
+    S_pad = sage_padded_len(S)
+    codes = np.empty((B, H, D, S_pad), dtype=np.uint8)
+    scales = np.empty((B, H, D), dtype=np.float32)
+    _check(_lib().oracle_quant_v(_ptr(v, ctypes.c_uint16), B, S, H, D, S_pad,
+                                 _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_float)),
+           "oracle_quant_v")
+    return codes, scales
+
+
+def sage_prepare(q, k, v, scale):
+    """The full prepare stage: (q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale)."""
+    qc, qs = quant_qk(q, q_multiplier(scale))
+    kc, ks = quant_qk(k, 1.0)
+    vc, vs = quant_v(v)
+    return qc, qs, kc, ks, vc, vs

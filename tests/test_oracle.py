@@ -1,0 +1,323 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Exact attention ("Kernel acceleration: attention, compilation and fusion",
+section "Attention: from O(N^2) memory to blocks") is pinned by invariants of
+softmax attention, closed forms at S = 1 and S = 2, the page's own blocked
+form, and PyTorch's scaled_dot_product_attention in float64 as an independent
+library routine.  The quantizer ("gfx1201_sage_prepare /
+gfx1201_sage_attention", section "Technical Details") is pinned by hand-made
+blocks with known codes, the OCP E4M3 value table and torch's float8_e4m3fn
+conversion.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from image_dit_amd import synth
+
+SCALE = float(np.float32(1.0 / math.sqrt(128.0)))
+
+
+def bf16(x):
+    return torch.as_tensor(x, dtype=torch.float32).to(torch.bfloat16)
+
+
+def rand_qkv(B, S, H, D=128, seed=0):
+    return synth.make_qkv(B, S, H, D, seed=seed)
+
+
+def f64(x):
+    return x.to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------------
+# exact attention
+# --------------------------------------------------------------------------
+
+def test_softmax_rows_sum_to_one():
+    q, k, _ = rand_qkv(1, 97, 2, seed=1)
+    for (h, i) in [(0, 0), (1, 50), (0, 96)]:
+        p = oracle.softmax_row(q, k, SCALE, 0, h, i)
+        assert p.min() >= 0.0
+        assert abs(p.sum() - 1.0) < 1e-12
+
+
+def test_constant_v_returns_v():
+    B, S, H, D = 2, 65, 3, 128
+    q, k, _ = rand_qkv(B, S, H, D, seed=2)
+    u = torch.randn((1, 1, H, D), generator=torch.Generator().manual_seed(3))
+    v = bf16(u.expand(B, S, H, D).contiguous())
+    out = oracle.attn_rows(q, k, v, SCALE)
+    ref = np.broadcast_to(f64(v[:, :1]), out.shape)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_identical_keys_give_mean_of_v():
+    B, S, H, D = 1, 80, 2, 128
+    q, _, v = rand_qkv(B, S, H, D, seed=4)
+    k1 = torch.randn((B, 1, H, D), generator=torch.Generator().manual_seed(5))
+    k = bf16(k1.expand(B, S, H, D).contiguous())
+    out = oracle.attn_rows(q, k, v, SCALE)
+    mean_v = f64(v).mean(axis=1, keepdims=True)
+    assert np.max(np.abs(out - mean_v)) < 1e-12
+
+
+def test_per_row_shift_of_all_keys_is_a_noop():
+    # k_j + w for one vector w and every key j shifts each score row by the
+    # constant q.w * scale, which the softmax removes.  Values are multiples
+    # of 1/16 below 8 in magnitude, so k + w is exact in BF16.
+    B, S, H, D = 1, 70, 2, 128
+    g = torch.Generator().manual_seed(6)
+    q = bf16(torch.randint(-32, 33, (B, S, H, D), generator=g) / 16.0)
+    k = bf16(torch.randint(-64, 65, (B, S, H, D), generator=g) / 16.0)
+    w = torch.randint(-64, 65, (1, 1, H, D), generator=g) / 16.0
+    v = bf16(torch.randn((B, S, H, D), generator=g))
+    k_shift = bf16(k.float() + w)
+    assert torch.equal(k_shift.float(), k.float() + w)  # exact
+    a = oracle.attn_rows(q, k, v, SCALE)
+    b = oracle.attn_rows(q, k_shift, v, SCALE)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_token_permutations():
+    B, S, H, D = 1, 90, 2, 128
+    q, k, v = rand_qkv(B, S, H, D, seed=7)
+    base = oracle.attn_rows(q, k, v, SCALE)
+    g = torch.Generator().manual_seed(8)
+    pq = torch.randperm(S, generator=g)
+    out_q = oracle.attn_rows(q[:, pq].contiguous(), k, v, SCALE)
+    assert np.max(np.abs(out_q - base[:, pq.numpy()])) < 1e-13
+    pk = torch.randperm(S, generator=g)
+    out_kv = oracle.attn_rows(q, k[:, pk].contiguous(), v[:, pk].contiguous(), SCALE)
+    assert np.max(np.abs(out_kv - base)) < 1e-12
+    # token order reversal of K/V together, as in the noise-floor run
+    rev = torch.arange(S - 1, -1, -1)
+    out_rev = oracle.attn_rows(q, k[:, rev].contiguous(), v[:, rev].contiguous(), SCALE)
+    assert np.max(np.abs(out_rev - base)) < 1e-12
+
+
+def test_single_key_returns_its_value():
+    q, k, v = rand_qkv(2, 1, 3, seed=9)
+    out = oracle.attn_rows(q, k, v, SCALE)
+    assert np.array_equal(out, f64(v))
+
+
+def test_two_keys_closed_form():
+    # o = sigmoid(d) v0 + sigmoid(-d) v1 with d = s0 - s1.
+    B, S, H, D = 1, 2, 2, 128
+    q, k, v = rand_qkv(B, S, H, D, seed=10)
+    out = oracle.attn_rows(q, k, v, SCALE)
+    qd, kd, vd = f64(q), f64(k), f64(v)
+    for i in range(S):
+        for h in range(H):
+            s0 = float(np.dot(qd[0, i, h], kd[0, 0, h])) * SCALE
+            s1 = float(np.dot(qd[0, i, h], kd[0, 1, h])) * SCALE
+            dlt = s0 - s1
+            sig = 1.0 / (1.0 + math.exp(-dlt))
+            ref = sig * vd[0, 0, h] + (1.0 - sig) * vd[0, 1, h]
+            assert np.max(np.abs(out[0, i, h] - ref)) < 1e-13
+
+
+@pytest.mark.parametrize("bq,bk", [(64, 64), (16, 256), (33, 7), (256, 16)])
+def test_blocked_form_matches_naive(bq, bk):
+    B, S, H, D = 2, 123, 2, 128
+    q, k, v = rand_qkv(B, S, H, D, seed=11)
+    a = oracle.attn_rows(q, k, v, SCALE)
+    b = oracle.attn_blocked(q, k, v, SCALE, bq=bq, bk=bk)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_matches_torch_sdpa_float64():
+    B, S, H, D = 2, 150, 3, 128
+    q, k, v = rand_qkv(B, S, H, D, seed=12)
+    out = oracle.attn_rows(q, k, v, SCALE)
+    t = lambda x: x.to(torch.float64).permute(0, 2, 1, 3).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), scale=SCALE)
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_sampled_rows_agree_with_full():
+    B, S, H, D = 2, 100, 3, 128
+    q, k, v = rand_qkv(B, S, H, D, seed=13)
+    full = oracle.attn_rows(q, k, v, SCALE)
+    rows = synth.sample_rows(B, S, H, n=200, seed=14)
+    part = oracle.attn_rows(q, k, v, SCALE, rows=rows)
+    assert np.array_equal(part, full[rows[:, 0], rows[:, 2], rows[:, 1]])
+
+
+def test_scale_enters_once():
+    # Doubling the scale equals doubling Q when Q doubles exactly.
+    q, k, v = rand_qkv(1, 40, 1, seed=15)
+    a = oracle.attn_rows(q, k, v, 2 * SCALE)
+    b = oracle.attn_rows(bf16(q.float() * 2), k, v, SCALE)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_row_sampler_forces_tail_rows():
+    rows = synth.sample_rows(1, 76112, 40, n=4096, seed=1006)
+    assert rows.shape == (4096, 3)
+    assert len({tuple(r) for r in rows.tolist()}) == 4096
+    tail = {(0, 0, i) for i in range(76112 - 32, 76112)} | {(0, 39, i) for i in range(76112 - 32, 76112)}
+    assert tail <= {tuple(r) for r in rows.tolist()}
+
+
+# --------------------------------------------------------------------------
+# quantizer
+# --------------------------------------------------------------------------
+
+E4M3_TABLE = [  # (value, code) from the OCP E4M3 definition: bias 7, 3 mantissa bits, max 448
+    (448.0, 0x7E), (1.0, 0x38), (2.0 ** -9, 0x01), (2.0 ** -6, 0x08), (-1.0, 0xB8),
+    (1.0625, 0x38), (1.1875, 0x3A), (464.0, 0x7E), (240.0, 0x77), (0.0, 0x00),
+    (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (-3 * 2.0 ** -10, 0x82), (256.0, 0x78),
+]
+
+
+@pytest.mark.parametrize("x,code", E4M3_TABLE)
+def test_e4m3_known_codes(x, code):
+    assert oracle.e4m3_encode(x) == code
+
+
+def test_e4m3_decode_table():
+    vals = [oracle.e4m3_decode(c) for c in range(127)]
+    assert vals[0] == 0.0 and vals[1] == 2.0 ** -9 and vals[8] == 2.0 ** -6 and vals[126] == 448.0
+    assert all(a < b for a, b in zip(vals, vals[1:]))  # strictly increasing
+    assert math.isnan(oracle.e4m3_decode(0x7F))
+    for c in range(127):
+        assert oracle.e4m3_encode(vals[c]) == c
+        assert oracle.e4m3_encode(-vals[c]) == 0x80 | c
+
+
+def test_e4m3_matches_torch_float8_e4m3fn():
+    vals = np.array([oracle.e4m3_decode(c) for c in range(127)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    xs = [vals, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+          np.nextafter(mids.astype(np.float32), np.float32(1000))]
+    allbf = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float().numpy()
+    xs.append(allbf[np.isfinite(allbf) & (np.abs(allbf) <= 448)])
+    xs.append(np.random.default_rng(0).uniform(-448, 448, 20000))
+    x = np.concatenate([np.concatenate(xs), -np.concatenate(xs)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
+
+
+def _put_block(values, S=32, H=1, D=128, h=0, rows=None):
+    x = torch.zeros((1, S, H, D), dtype=torch.float32)
+    flat = x[0, :32, h].reshape(-1)
+    flat[: len(values)] = torch.tensor(values, dtype=torch.float32)
+    x[0, :32, h] = flat.reshape(32, D)
+    return bf16(x)
+
+
+def test_quant_round_half_even_at_unit_scale():
+    vals = [127.0, 2.5, 3.5, -0.5, -1.5, 0.5, -2.5, 1.25, -126.5]
+    codes, scales = oracle.quant_qk(_put_block(vals), 1.0)
+    assert scales[0, 0, 0] == np.float32(1.0)
+    assert scales.shape == (1, 1, 8)  # S_pad = 256
+    assert list(codes[0, 0, 0, :9]) == [127, 2, 4, 0, -2, 0, -2, 1, -126]
+    assert not codes[0, 0, 0, 9:].any() and not codes[0, 0, 1:].any()
+    assert np.all(scales[0, 0, 1:] == 0)
+
+
+def test_quant_absmax_maps_to_127_and_error_bound():
+    q, k, _ = rand_qkv(2, 300, 3, seed=16)
+    for x, mult in ((k, 1.0), (q, oracle.q_multiplier(SCALE))):
+        codes, scales = oracle.quant_qk(x, mult)
+        S_pad = codes.shape[2]
+        assert S_pad == 512
+        y = (x.float() * np.float32(mult)).numpy().astype(np.float32)  # [B,S,H,D]
+        y = np.transpose(y, (0, 2, 1, 3))  # [B,H,S,D]
+        for b in range(2):
+            for h in range(3):
+                for blk in range(S_pad // 32):
+                    c = codes[b, h, blk * 32:(blk + 1) * 32].astype(np.float64)
+                    s = float(scales[b, h, blk])
+                    yb = y[b, h, blk * 32:min(blk * 32 + 32, 300)]
+                    if yb.shape[0] == 0:
+                        assert s == 0.0 and not c.any()
+                        continue
+                    amax = np.abs(yb).max()
+                    assert s == np.float32(np.float32(amax) / np.float32(127.0))
+                    arg = np.unravel_index(np.argmax(np.abs(yb)), yb.shape)
+                    assert abs(c[arg]) == 127
+                    err = np.abs(yb - c[: yb.shape[0]] * s)
+                    assert err.max() <= s / 2 * (1 + 1e-5)
+                    assert not c[yb.shape[0]:].any()  # pad rows
+
+
+def test_quant_zero_block():
+    x = bf16(torch.zeros((1, 64, 1, 128)))
+    codes, scales = oracle.quant_qk(x, 1.0)
+    assert not codes.any() and not scales.any()
+    vcodes, vscales = oracle.quant_v(x)
+    assert not vcodes.any() and not vscales.any()
+
+
+def test_q_multiplier_is_scale_times_log2e():
+    c = oracle.q_multiplier(SCALE)
+    # float32(1/sqrt(128)) / ln 2 rounded once to fp32 (an independent route)
+    assert np.float32(c) == np.float32(np.float64(np.float32(1 / math.sqrt(128))) / math.log(2.0))
+    assert np.float32(c).view(np.uint32) == 0x3E0293EE
+
+
+def test_quant_matches_torch_vectorized():
+    q, k, _ = rand_qkv(1, 200, 2, seed=17)
+    for x, mult in ((k, 1.0), (q, oracle.q_multiplier(SCALE))):
+        codes, scales = oracle.quant_qk(x, mult)
+        y = (x.float() * torch.tensor(mult, dtype=torch.float32)).permute(0, 2, 1, 3)
+        y = torch.nn.functional.pad(y, (0, 0, 0, 256 - 200))
+        blocks = y.reshape(1, 2, 8, 32, 128)
+        amax = blocks.abs().amax(dim=(-1, -2))
+        s = amax / torch.tensor(127.0)
+        ref = torch.where(s[..., None, None] > 0, torch.round(blocks / s[..., None, None]), torch.zeros(()))
+        ref = ref.clamp(-127, 127).to(torch.int8).reshape(1, 2, 256, 128)
+        assert np.array_equal(scales, s.numpy())
+        assert np.array_equal(codes, ref.numpy())
+
+
+def test_quant_v_transpose_and_scales():
+    B, S, H, D = 1, 300, 2, 128
+    _, _, v = rand_qkv(B, S, H, D, seed=18)
+    codes, scales = oracle.quant_v(v)
+    assert codes.shape == (1, 2, 128, 512) and scales.shape == (1, 2, 128)
+    vf = v.float().numpy()
+    amax = np.abs(vf).max(axis=1)  # [B,H,D]
+    assert np.array_equal(scales, (amax / np.float32(448.0)).astype(np.float32))
+    ref = (torch.from_numpy(vf / scales[:, None, :, :]).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    assert np.array_equal(codes[:, :, :, :S], np.transpose(ref, (0, 2, 3, 1)))
+    assert not codes[:, :, :, S:].any()
+    # the absmax token of every channel reaches the largest code
+    top = np.abs(vf).argmax(axis=1)
+    for h in range(H):
+        for ch in range(D):
+            assert codes[0, h, ch, top[0, h, ch]] & 0x7F == 0x7E
+
+
+# --------------------------------------------------------------------------
+# cost model against the table the handbook page prints
+# --------------------------------------------------------------------------
+
+def test_cost_model_reproduces_printed_table():
+    import json
+    import os
+    from image_dit_amd import cost
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "attn_cost_table.json")))
+    GiB = 1024.0 ** 3
+    for row in g["attn_bytes_rows"]:
+        n, h = row["tokens"], row["heads"]
+        assert round(cost.score_matrix_bytes(1, h, n) / GiB, 1) == row["scores_gib"]
+        assert round(cost.naive_attn_bytes(1, h, n, 128) / GiB, 1) == row["naive_gib"]
+        assert round(cost.attn_bytes_bf16(1, h, n, 128) / GiB, 2) == row["flash_gib"]
+    fr = g["flash_block_profile_row"]
+    heads = fr["d_model"] // 128
+    flops = cost.attn_flops(1, heads, fr["n"], 128)
+    byts = cost.attn_bytes_bf16(1, heads, fr["n"], 128)
+    assert round(flops / 1e9, 1) == fr["gflop"]
+    assert round(byts / 2 ** 20) == fr["traffic_mib"]
+    assert round(flops / byts) == fr["intensity"]
+    assert round(max(flops / fr["peak_flops"], byts / fr["bandwidth"]) * 1e6) == fr["time_us"]
