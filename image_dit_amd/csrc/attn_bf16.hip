@@ -1,0 +1,265 @@
+// attn_bf16.hip -- BF16 flash self-attention forward for gfx950 (MI355X).
+//
+// Operation: "Kernel acceleration: attention, compilation and fusion",
+// section "Attention: from O(N^2) memory to blocks" -- attention computed one
+// key block at a time with a running row max m, running row sum l and an
+// accumulator rescaled by exp(m_old - m_new), so the S x S scores never leave
+// the chip.  Shape contract (BF16 [B, S, H, 128] in and out, non-causal) from
+// "gfx1201_sage_prepare / gfx1201_sage_attention", "Technical Details".
+//
+// gfx950 mapping
+//   * Work unit: one workgroup per (b, h, BQ-row query tile); 4 waves, each
+//     owning 32 * QG query rows.  Workgroups are remapped so one head's tiles
+//     share an XCD (and its L2) while they stream the same K/V.
+//   * Scores are computed transposed, S^T = K Q^T, on
+//     v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 channels read from LDS,
+//     B = 16 channels x 32 queries kept in registers for the whole loop.  In
+//     the accumulator every lane then owns ONE query row (column l % 32) and 16
+//     of its keys, so row max / row sum are per-lane loops plus one
+//     permlane32_swap with the other half-wave.
+//   * O^T = V^T P^T on the same MFMA: the accumulator registers of S^T, rounded
+//     to BF16, are exactly the B operand (same lane = same query, same keys),
+//     so P never goes through LDS.  The A operand V^T (channels x keys) is read
+//     from the row-major V tile with ds_read_b64_tr_b16, which transposes 16-bit
+//     elements inside groups of 16 lanes.
+//   * K/V tiles of BK = 64 keys are double-buffered in LDS (one barrier per
+//     tile).  Rows are 256 B, unpadded, with 16-byte chunks XOR-swizzled per row
+//     so that both the MFMA-operand reads and the transposed reads are free of
+//     bank conflicts.
+//   * Softmax in base 2: x = s * c with c = scale * log2(e); exp2 on v_exp_f32.
+//     The running max is only raised when a row's tile max exceeds it by more
+//     than kLazyThresh (in log2 units): P values up to 2^kLazyThresh are
+//     harmless in BF16/FP32, and the O rescale (64 multiplies per lane and
+//     query group) is skipped on almost every tile.  The result is the same
+//     math: every p and l use the same stale max, which cancels in acc / l.
+//   * Ragged tail: key rows >= S are zero-filled in LDS and their scores set to
+//     -inf; query rows >= S are computed on zeros and not stored.
+#include "common.hpp"
+
+namespace ditattn {
+namespace bf16attn {
+
+constexpr int BK = 64;      // keys per K/V tile
+constexpr int NW = 4;       // waves per workgroup
+constexpr int ROW_CHUNKS = 16;  // 16-byte chunks per 128-channel BF16 row
+constexpr float kLazyThresh = 8.0f;
+
+// chunk index (16 B units) of (row, chunk) inside a K or V tile
+__device__ __forceinline__ int k_chunk(int row, int c) { return row * ROW_CHUNKS + (c ^ (row & 15)); }
+__device__ __forceinline__ int v_chunk(int row, int c) { return row * ROW_CHUNKS + (c ^ ((row & 3) << 2)); }
+
+template <int QG>
+__global__ void __launch_bounds__(NW * 64)
+attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                     const __bf16* __restrict__ v, __bf16* __restrict__ o, int S, int H, float c,
+                     int num_qt, int n_tiles) {
+  constexpr int BQ = NW * QG * 32;
+  __shared__ __attribute__((aligned(16))) uint4 lds_k[2][BK * ROW_CHUNKS];
+  __shared__ __attribute__((aligned(16))) uint4 lds_v[2][BK * ROW_CHUNKS];
+
+  const int L = xcd_remap(blockIdx.x, n_tiles);
+  const int bh = L / num_qt;
+  const int qt = L - bh * num_qt;
+  const int b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, l = tid & 63, hl = l >> 5, ln = l & 31;
+  const int64_t tok = (int64_t)H * kHeadDim;  // elements between consecutive tokens
+  const int64_t base = ((int64_t)b * S * H + h) * kHeadDim;
+  const __bf16* qbh = q + base;
+  const __bf16* kbh = k + base;
+  const __bf16* vbh = v + base;
+  __bf16* obh = o + base;
+
+  // Q^T operand, resident for the whole key loop: Q[q0 + 32 g + ln][16 ks + 8 hl + 0..7].
+  const int q0 = qt * BQ + wave * QG * 32;
+  bf16x8 qf[QG][8];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const int i = q0 + 32 * g + ln;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (i < S) qf[g][ks] = *(const bf16x8*)(qbh + i * tok + 16 * ks + 8 * hl);
+      else qf[g][ks] = bf16x8{};
+    }
+  }
+
+  f32x16 acc[QG][4];
+  float m[QG], lsum[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    m[g] = -INFINITY;
+    lsum[g] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[g][dt] = f32x16{};
+  }
+
+  // Staging: thread tid moves chunk (tid & 15) of rows (tid >> 4) + 16 p, p = 0..3.
+  const int st_row = tid >> 4, st_chunk = tid & 15;
+  uint4 kst[4], vst[4];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int j = t * BK + st_row + 16 * p;
+      if (j < S) {
+        kst[p] = *(const uint4*)(kbh + j * tok + 8 * st_chunk);
+        vst[p] = *(const uint4*)(vbh + j * tok + 8 * st_chunk);
+      } else {
+        kst[p] = uint4{0, 0, 0, 0};
+        vst[p] = uint4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      lds_k[buf][k_chunk(st_row + 16 * p, st_chunk)] = kst[p];
+      lds_v[buf][v_chunk(st_row + 16 * p, st_chunk)] = vst[p];
+    }
+  };
+
+  const int n_kt = (S + BK - 1) / BK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_kt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_kt) load_tile(t + 1);
+
+    // ---- S^T = K Q^T for 64 keys x 32 QG queries
+    f32x16 s[2][QG];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int g = 0; g < QG; ++g) s[tt][g] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_k[buf][k_chunk(32 * tt + ln, 2 * ks + hl)]);
+#pragma unroll
+        for (int g = 0; g < QG; ++g) s[tt][g] = mfma_bf16_32x32x16(kf, qf[g][ks], s[tt][g]);
+      }
+    }
+
+    // ---- mask keys >= S (only the last, partial tile)
+    const int j0 = t * BK;
+    if (j0 + BK > S) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * tt + 8 * (r >> 2) + 4 * hl + (r & 3);
+#pragma unroll
+          for (int g = 0; g < QG; ++g)
+            if (j >= S) s[tt][g][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (base 2), P -> BF16 B operands
+    bf16x8 pf[QG][4];
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      float mx = s[0][g][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][g][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][g][r]);
+      mx = half_pair_max(mx) * c;
+      // raise the running max only when it grew by more than the threshold
+      if (__builtin_amdgcn_ballot_w64(mx > m[g] + kLazyThresh) != 0) {
+        const float m_new = fmaxf(m[g], mx);
+        const float alpha = fast_exp2(m[g] - m_new);
+        m[g] = m_new;
+        lsum[g] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[g][dt] *= alpha;
+      }
+      const float mneg = -m[g];
+      float ps = 0.0f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = fast_exp2(fmaf(s[tt][g][8 * half + e], c, mneg));
+            ps += p[e];
+          }
+          bf16x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = (__bf16)p[e];
+          pf[g][2 * tt + half] = pv;
+        }
+      }
+      lsum[g] += ps;
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        // lane l, element e of A = V[16 cc + 8 (e / 4) + 4 hl + e % 4][32 dt + ln]
+        const int grp = l >> 4, j = l & 15;
+        const int col = 32 * dt + 16 * (grp & 1) + 4 * (j & 3);  // BF16 column
+        i16x4 part[2];
+#pragma unroll
+        for (int E = 0; E < 2; ++E) {
+          const int row = 16 * cc + 8 * E + 4 * hl + (j >> 2);
+          const int byte = v_chunk(row, col >> 3) * 16 + (col & 7) * 2;
+          part[E] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (DITATTN_LDS i16x4*)((DITATTN_LDS char*)&lds_v[buf][0] + byte));
+        }
+        // whole-vector casts only: element-wise bf16 <-> i16 bit casts are not
+        // lowered reliably by this compiler
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int g = 0; g < QG; ++g) acc[g][dt] = mfma_bf16_32x32x16(va, pf[g][cc], acc[g][dt]);
+      }
+    }
+
+    if (t + 1 < n_kt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, BF16, rows < S
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const float inv = 1.0f / half_pair_sum(lsum[g]);
+    const int i = q0 + 32 * g + ln;
+    if (i < S) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d = 32 * dt + 8 * rq + 4 * hl;
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[g][dt][4 * rq + e] * inv);
+          *(bf16x4*)(obh + i * tok + d) = ov;
+        }
+    }
+  }
+}
+
+}  // namespace bf16attn
+
+// Query rows per workgroup of the launched configuration.
+constexpr int kBf16QG = 1;
+constexpr int kBf16BQ = bf16attn::NW * kBf16QG * 32;
+
+int bf16_tile_rows() { return kBf16BQ; }
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B,
+                                int S, int H, float c, hipStream_t stream) {
+  const int num_qt = (S + kBf16BQ - 1) / kBf16BQ;
+  const int n_tiles = B * H * num_qt;
+  hipLaunchKernelGGL(bf16attn::attn_fwd_bf16_kernel<kBf16QG>, dim3(n_tiles), dim3(bf16attn::NW * 64),
+                     0, stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, S,
+                     H, c, num_qt, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace ditattn

@@ -1,0 +1,85 @@
+// common.hpp -- device helpers shared by the gfx950 attention kernels.
+//
+// MFMA operand/accumulator layouts used throughout (CDNA3/CDNA4 32x32 MFMA,
+// checked on gfx950 with an in-bounds probe):
+//   A (M x K): lane l holds row m = l % 32, a run of K-elements chosen by l / 32
+//   B (K x N): lane l holds column n = l % 32, the same K-elements as A
+//   D (M x N): lane l, accumulator register r holds
+//              row m = 8 * (r / 4) + 4 * (l / 32) + (r % 4), column n = l % 32.
+// Because A and B draw the same K-elements from the same lane, only the
+// accumulator layout matters for correctness; the K order inside a lane is
+// free as long as both operands use it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ditattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+#define DITATTN_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+// Value of `x` held by lane l ^ 32 (the other half of the wavefront).
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // lanes 0..31 receive the upper half's value in r[1], lanes 32..63 the lower half's in r[0]
+  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
+}
+
+// max / sum of x over lanes l and l ^ 32.
+__device__ __forceinline__ float half_pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round two fp32 values to BF16 (nearest even) and pack them, low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ i32x16 mfma_i8_32x32x32(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+// FP8 (OCP e4m3) x FP8 -> FP32, 32x32x64; block scales fixed at 2^0.
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Workgroup index remapped so that consecutive logical tiles land on the same
+// XCD: the dispatcher deals workgroups round-robin over the 8 XCDs, so
+// physical block w runs on XCD w % 8.  Logical tiles [prefix(x), prefix(x+1))
+// go to XCD x; tiles of one head then share that XCD's L2 for K/V.
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int x = w & 7, slot = w >> 3;
+  const int q = n >> 3, rem = n & 7;
+  return x * q + (x < rem ? x : rem) + slot;
+}
+
+}  // namespace ditattn

@@ -1,0 +1,230 @@
+// prepare.hip -- Sage prepare stage for gfx950: BF16 Q/K -> INT8 codes with
+// one FP32 scale per (b, h, 32-row block), V -> FP8 e4m3 codes with one FP32
+// scale per (b, h, channel), transposed to [B, H, 128, S_pad].
+//
+// Operation: "gfx1201_sage_prepare / gfx1201_sage_attention" (aiter PR 6390),
+// first commit and "Technical Details".  Q carries softmax_scale * log2(e):
+// it is multiplied by c = float(double(scale) * log2(e)) in fp32 before it is
+// quantized.  Scales are absmax / 127 (Q, K) and absmax / 448 (V, the largest
+// finite e4m3 value); codes round to nearest even; an all-zero block or
+// channel gets scale 0 and codes 0; pad rows, pad tokens and pad blocks are 0.
+//
+// All of it is HBM-bound, so the kernels are shaped for coalescing:
+//   quant_qk   one wave per (b, h, 32-row block) of Q or K: 32 rows x 256 B in,
+//              4 KB of codes out (contiguous), one scale.
+//   v_absmax   per (b, 256-token chunk): every thread keeps the running |v| max
+//              of 8 channels over the chunk (rows are H x 256 B contiguous),
+//              then one atomicMax per channel on the fp32 bit pattern (order
+//              free: max of non-negative floats = max of their bit patterns).
+//   v_quant    per (b, h, 128-token chunk): quantize, transpose through LDS,
+//              write 128 channel rows of 128 B.
+//   v_finalize v_scale = absmax / 448 in place.
+// Division and rounding are IEEE fp32 (the library is built with correctly
+// rounded division), so the codes are bit-identical to a scalar CPU quantizer.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ditattn {
+namespace prep {
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+// ---------------------------------------------------------------- Q and K
+// grid.x: ceil(B * H * nblk / 4) workgroups of 4 waves; grid.y: 0 = Q, 1 = K.
+__global__ void __launch_bounds__(256)
+quant_qk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                int8_t* __restrict__ q_i8, float* __restrict__ q_scale, int8_t* __restrict__ k_i8,
+                float* __restrict__ k_scale, int S, int H, int nblk, int units, float c) {
+  const bool is_q = blockIdx.y == 0;
+  const uint16_t* x = is_q ? q : k;
+  int8_t* codes = is_q ? q_i8 : k_i8;
+  float* scales = is_q ? q_scale : k_scale;
+  const float mult = is_q ? c : 1.0f;  // x * 1.0f is exact
+
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= units) return;
+  const int lane = threadIdx.x & 63;
+  const int blk = unit % nblk;
+  const int bh = unit / nblk;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t tok = (int64_t)H * kHeadDim;
+  const uint16_t* src = x + ((int64_t)b * S * H + h) * kHeadDim;
+
+  // lane owns 8 channels (chunk lane & 15) of rows (lane >> 4) + 4 p, p = 0..7
+  const int chunk = lane & 15;
+  float y[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int i = blk * 32 + (lane >> 4) + 4 * p;
+    uint4 raw = uint4{0, 0, 0, 0};
+    if (i < S) raw = *(const uint4*)(src + i * tok + 8 * chunk);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[p][2 * e] = bf16_bits_to_f32(w[e] & 0xFFFFu) * mult;
+      y[p][2 * e + 1] = bf16_bits_to_f32(w[e] >> 16) * mult;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[p][e]));
+  }
+  amax = wave_max(amax);
+  const float s = amax / 127.0f;
+  int8_t* dst = codes + ((int64_t)bh * nblk * 32 + blk * 32) * kHeadDim;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = (lane >> 4) + 4 * p;
+    uint32_t packed[2] = {0u, 0u};
+    if (s != 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float qv = rintf(y[p][e] / s);
+        qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+        packed[e >> 2] |= ((uint32_t)(int)qv & 0xFFu) << (8 * (e & 3));
+      }
+    }
+    *(uint2*)(dst + r * kHeadDim + 8 * chunk) = uint2{packed[0], packed[1]};
+  }
+  if (lane == 0) scales[(int64_t)bh * nblk + blk] = s;
+}
+
+// ---------------------------------------------------------------- V absmax
+constexpr int kAbsTok = 256;  // tokens per v_absmax workgroup
+
+__global__ void __launch_bounds__(256)
+fill_zero_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// grid (ceil(S / kAbsTok), ceil(H * 16 / 256), B); amax_bits: [B, H, 128] fp32
+// bit patterns, zeroed.  Thread -> one 16-byte chunk column (8 channels of one
+// head) over kAbsTok tokens, 8 loads in flight.
+__global__ void __launch_bounds__(256)
+v_absmax_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits, int S, int H) {
+  const int b = blockIdx.z;
+  const int col = blockIdx.y * 256 + threadIdx.x;
+  const int ncol = H * 16;  // 16-byte chunks per token row (all heads)
+  if (col >= ncol) return;
+  const int j0 = blockIdx.x * kAbsTok;
+  const int j1 = min(j0 + kAbsTok, S);
+  const int64_t tok = (int64_t)H * kHeadDim;
+  const uint16_t* src = v + (int64_t)b * S * tok + 8 * col;
+  uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // |v| as bf16 magnitude bits
+  for (int j = j0; j < j1; j += 8) {
+    uint4 raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) raw[u] = (j + u < j1) ? *(const uint4*)(src + (j + u) * tok) : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mx[2 * e] = max(mx[2 * e], w[e] & 0x7FFFu);
+        mx[2 * e + 1] = max(mx[2 * e + 1], (w[e] >> 16) & 0x7FFFu);
+      }
+    }
+  }
+  // bf16 magnitude bits << 16 = fp32 bits of |v|; finite magnitudes order like integers
+  uint32_t* dst = amax_bits + (int64_t)b * H * kHeadDim + 8 * col;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (mx[e] != 0u) atomicMax(dst + e, mx[e] << 16);
+}
+
+// ---------------------------------------------------------------- V quantize + transpose
+constexpr int kVTok = 128;          // tokens per v_quant workgroup
+constexpr int kVRowB = kVTok + 8;   // LDS row stride in bytes (channel rows)
+
+// grid (S_pad / kVTok, B * H).  Thread t: chunk t & 15 (8 channels), tokens 8 * (t >> 4) + 0..7.
+__global__ void __launch_bounds__(256)
+v_quant_kernel(const uint16_t* __restrict__ v, const uint32_t* __restrict__ amax_bits,
+               uint8_t* __restrict__ v_fp8, int S, int H, int S_pad) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kHeadDim * kVRowB];
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const int j0 = blockIdx.x * kVTok;
+  const int chunk = threadIdx.x & 15, tg = threadIdx.x >> 4;
+  const int64_t tok = (int64_t)H * kHeadDim;
+  const uint16_t* src = v + ((int64_t)b * S * H + h) * kHeadDim;
+
+  float sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sv[e] = __uint_as_float(amax_bits[(int64_t)bh * kHeadDim + 8 * chunk + e]) / 448.0f;
+
+  float x[8][8];  // [token][channel]
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int j = j0 + 8 * tg + u;
+    uint4 raw = uint4{0, 0, 0, 0};
+    if (j < S) raw = *(const uint4*)(src + j * tok + 8 * chunk);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[u][2 * e] = bf16_bits_to_f32(w[e] & 0xFFFFu);
+      x[u][2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {  // channel 8 * chunk + e, tokens 8 tg + 0..7
+    uint32_t word[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + 8 * tg + 4 * half + u;
+        a[u] = (j < S && sv[e] != 0.0f) ? x[4 * half + u][e] / sv[e] : 0.0f;
+      }
+      int wv = __builtin_amdgcn_cvt_pk_fp8_f32(a[0], a[1], 0, false);
+      wv = __builtin_amdgcn_cvt_pk_fp8_f32(a[2], a[3], wv, true);
+      word[half] = (uint32_t)wv;
+    }
+    *(uint2*)(lds + (8 * chunk + e) * kVRowB + 8 * tg) = uint2{word[0], word[1]};
+  }
+  __syncthreads();
+  // 128 channel rows x 128 B; 8 bytes per thread per step, 16 threads per row
+  uint8_t* dst = v_fp8 + (int64_t)bh * kHeadDim * S_pad + j0;
+#pragma unroll
+  for (int step = 0; step < 8; ++step) {
+    const int idx = step * 256 + threadIdx.x;
+    const int row = idx >> 4, part = idx & 15;
+    *(uint2*)(dst + (int64_t)row * S_pad + 8 * part) = *(const uint2*)(lds + row * kVRowB + 8 * part);
+  }
+}
+
+__global__ void __launch_bounds__(256)
+v_finalize_kernel(float* __restrict__ v_scale, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) v_scale[i] = v_scale[i] / 448.0f;  // absmax bits read as fp32
+}
+
+}  // namespace prep
+
+hipError_t launch_sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8,
+                               float* q_scale, int8_t* k_i8, float* k_scale, uint8_t* v_fp8,
+                               float* v_scale, int B, int S, int H, int S_pad, float c,
+                               hipStream_t stream) {
+  const int nblk = S_pad / 32;
+  const int units = B * H * nblk;
+  const int nscale = B * H * kHeadDim;
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(v_scale);
+  hipLaunchKernelGGL(prep::fill_zero_kernel, dim3((nscale + 255) / 256), dim3(256), 0, stream, amax_bits, nscale);
+  hipLaunchKernelGGL(prep::quant_qk_kernel, dim3((units + 3) / 4, 2), dim3(256), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, q_i8, q_scale, k_i8, k_scale, S, H, nblk,
+                     units, c);
+  hipLaunchKernelGGL(prep::v_absmax_kernel, dim3((S + prep::kAbsTok - 1) / prep::kAbsTok, (H * 16 + 255) / 256, B),
+                     dim3(256), 0, stream, (const uint16_t*)v, amax_bits, S, H);
+  hipLaunchKernelGGL(prep::v_quant_kernel, dim3(S_pad / prep::kVTok, B * H), dim3(256), 0, stream,
+                     (const uint16_t*)v, (const uint32_t*)amax_bits, v_fp8, S, H, S_pad);
+  hipLaunchKernelGGL(prep::v_finalize_kernel, dim3((nscale + 255) / 256), dim3(256), 0, stream, v_scale, nscale);
+  return hipGetLastError();
+}
+
+}  // namespace ditattn

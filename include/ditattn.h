@@ -1,0 +1,135 @@
+/*
+ * ditattn.h -- C ABI of the MI355X (gfx950) DiT flash self-attention library
+ * (libditattn.so).
+ *
+ * Non-causal self-attention forward at head dim 128, as used by diffusion
+ * transformers, in two modes:
+ *   - BF16: both GEMMs in BF16 on MFMA, FP32 accumulation, online softmax.
+ *   - Sage: a prepare stage quantizes Q/K to INT8 and V to FP8 e4m3; Q.K^T
+ *     then runs on INT8 MFMA and P.V on FP8 MFMA, FP32 accumulation.
+ *
+ * Sources of the operations (page title, section):
+ *   [FA]   "Kernel acceleration: attention, compilation and fusion",
+ *          section "Attention: from O(N^2) memory to blocks": attention
+ *          computed block by block with a running max and sum (online
+ *          softmax), never writing the N x N score matrix.
+ *   [SAGE] "gfx1201_sage_prepare / gfx1201_sage_attention" (aiter PR 6390),
+ *          sections "Technical Details" and the two commit messages: the
+ *          prepare stage and the quantized forward, non-causal, head dim 128,
+ *          no mask or varlen, BF16 in and out, forward only.
+ *   [RDNA] "RDNAttention" README, sections "Overview" and "Quick start": a
+ *          thin wrapper that hands the device pointers of existing tensors to
+ *          the kernel, with no staging copies and no second GPU context.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls and is thread-safe.
+ *   - Tensors are contiguous.  BF16 tensors q, k, v, o are [B, S, H, D]
+ *     (token-major, head next, channel fastest), 2 bytes per element.
+ *   - D must be 128.  B, S, H must be >= 1 and every byte size must fit in
+ *     int64 and the grid limits.
+ *   - Every pointer must be 16-byte aligned.
+ *   - Each call only enqueues work on `stream` (0 = the null stream) and
+ *     returns; results are valid once the stream has reached that point.
+ *     Nothing synchronizes the device.
+ *   - Errors are returned, never raised, printed or aborted on.  Arguments are
+ *     checked before anything is enqueued: an argument error leaves every
+ *     output untouched.  DITATTN_EHIP reports a failed launch (the HIP error
+ *     is cleared with hipGetLastError; outputs are then undefined).
+ *   - Padded length: S_pad = ditattn_sage_padded_len(S) = S rounded up to a
+ *     multiple of 256.
+ */
+#ifndef DITATTN_H
+#define DITATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same definition as the HIP runtime's, so both headers can be included. */
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+#define DITATTN_ABI_VERSION 1
+
+/* Status codes. */
+#define DITATTN_OK 0
+#define DITATTN_EINVAL (-1)       /* B, S or H < 1, null pointer, scale not finite or <= 0, output aliasing an input */
+#define DITATTN_EUNSUPPORTED (-2) /* D != 128 */
+#define DITATTN_EALIGN (-3)       /* a pointer is not 16-byte aligned */
+#define DITATTN_EOVERFLOW (-4)    /* a byte size or the grid exceeds what the kernels index */
+#define DITATTN_EHIP (-5)         /* the HIP runtime rejected a launch */
+
+/* DITATTN_ABI_VERSION of the loaded library. */
+int ditattn_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char* ditattn_status_string(int status);
+
+/* S rounded up to a multiple of 256 (the token length of prepared tensors);
+ * -1 if S < 1 or the result overflows int. */
+int ditattn_sage_padded_len(int S);
+
+/*
+ * attn_fwd_bf16 -- o = softmax(q k^T * scale) v per (batch, head), non-causal.
+ * [FA] (tiled online softmax); [SAGE] "Technical Details" (shape contract:
+ * BF16 [B, S, H, 128] in and out, non-causal, no mask).
+ *   q, k, v : const BF16 [B, S, H, 128]
+ *   o       : BF16 [B, S, H, 128], written in full; must not overlap q, k or v
+ *   scale   : softmax scale (e.g. 1/sqrt(128)), finite and > 0
+ * Softmax runs in FP32 in base 2 (scores times scale * log2(e)); P is rounded
+ * to BF16 for the second GEMM; the row sum uses the FP32 values.
+ */
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, int S, int H,
+                  int D, float scale, hipStream_t stream);
+
+/*
+ * sage_prepare -- quantize BF16 Q, K, V for sage_attn_fwd.  [SAGE] first
+ * commit and "Technical Details" (Q/K to INT8 with one FP32 scale per
+ * (batch, head, 32-row block), Q carrying scale * log2(e); V to FP8 e4m3
+ * with one FP32 scale per channel, transposed to [B, H, 128, S_pad]).
+ *   q, k, v  : const BF16 [B, S, H, 128]
+ *   q_i8     : int8  [B, H, S_pad, 128]  Q codes
+ *   q_scale  : float [B, H, S_pad / 32]  one scale per 32-row block
+ *   k_i8     : int8  [B, H, S_pad, 128]  K codes
+ *   k_scale  : float [B, H, S_pad / 32]
+ *   v_fp8    : uint8 [B, H, 128, S_pad]  V codes, OCP FP8 E4M3 (e4m3fn) bytes
+ *   v_scale  : float [B, H, 128]         one scale per (b, h, channel)
+ *   scale    : the softmax scale the attention will use, finite and > 0
+ * Arithmetic (IEEE fp32, round to nearest even throughout):
+ *   c = float(double(scale) * log2(e));  Q values y = float(q) * c, K values y = float(k)
+ *   per 32-row block: s = max|y| / 127, code = clamp(rint(y / s), -127, 127)
+ *   per V channel over the S real tokens: sv = max|v| / 448, code = e4m3(v / sv)
+ *   an all-zero block or channel gets scale 0 and codes 0; pad rows, pad
+ *   columns (tokens S..S_pad-1) and pad blocks are written as 0.
+ * Outputs must not overlap each other or the inputs.  v_scale doubles as the
+ * absmax scratch while the call runs.
+ */
+int sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8, float* q_scale,
+                 int8_t* k_i8, float* k_scale, uint8_t* v_fp8, float* v_scale, int B, int S,
+                 int H, int D, float scale, hipStream_t stream);
+
+/*
+ * sage_attn_fwd -- the quantized forward on tensors written by sage_prepare
+ * (the kernel alone on prepared tensors).  [SAGE] second commit: Q K^T on
+ * INT8 MFMA, P V on FP8 MFMA, FP32 accumulation, online softmax, BF16 out.
+ *   q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale : as written by sage_prepare
+ *                                                 for the same B, S, H
+ *   o      : BF16 [B, S, H, 128], written in full; must not overlap the inputs
+ *   scale  : checked (finite, > 0) but otherwise unused: sage_prepare already
+ *            folded scale * log2(e) into q_scale.
+ * Scores s = int32(q_code . k_code) * q_scale * k_scale are in base-2 units.
+ * Keys j >= S are masked.  P is rounded to FP8 e4m3 as p * 2^8; the row sum
+ * uses the FP32 values; o = acc * v_scale / (l * 2^8).
+ */
+int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                  const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
+                  int B, int S, int H, int D, float scale, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DITATTN_H */

@@ -253,17 +253,32 @@ double oracle_e4m3_decode(uint8_t code) {
  * binary search finds the two neighbours of |x| and the nearer one wins.
  * The sign bit is copied from x (so -0.0 and tiny negatives give 0x80).
  */
+static double e4m3_mag[127]; /* e4m3_mag[c] = oracle_e4m3_decode(c), filled once */
+static int e4m3_ready = 0;
+
+static void e4m3_fill(void) {
+#pragma omp critical(oracle_e4m3_table)
+  {
+    if (!e4m3_ready) {
+      for (int c = 0; c < 127; ++c) e4m3_mag[c] = oracle_e4m3_decode((uint8_t)c);
+#pragma omp flush
+      e4m3_ready = 1;
+    }
+  }
+}
+
 uint8_t oracle_e4m3_encode(float x) {
+  if (!e4m3_ready) e4m3_fill();
   const uint8_t sign = signbit(x) ? 0x80 : 0x00;
   const double a = fabs((double)x);
   if (a >= 448.0) return sign | 0x7E;
   int lo = 0, hi = 126; /* invariant: value(lo) <= a < value(hi) */
   while (hi - lo > 1) {
     const int mid = (lo + hi) / 2;
-    if (oracle_e4m3_decode((uint8_t)mid) <= a) lo = mid; else hi = mid;
+    if (e4m3_mag[mid] <= a) lo = mid; else hi = mid;
   }
-  const double dlo = a - oracle_e4m3_decode((uint8_t)lo);
-  const double dhi = oracle_e4m3_decode((uint8_t)hi) - a;
+  const double dlo = a - e4m3_mag[lo];
+  const double dhi = e4m3_mag[hi] - a;
   int code;
   if (dlo < dhi) code = lo;
   else if (dhi < dlo) code = hi;
@@ -287,6 +302,9 @@ int oracle_quant_qk(const uint16_t* x, int B, int S, int H, int D, float mult, i
                     int8_t* codes, float* scales) {
   if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || S_pad < S || S_pad % 32 != 0) return ORACLE_EINVAL;
   const int nblk = S_pad / 32;
+  int status = ORACLE_OK;
+  /* blocks are independent; spread them over the host cores */
+#pragma omp parallel for collapse(3) schedule(static)
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < H; ++h)
       for (int blk = 0; blk < nblk; ++blk) {
@@ -296,7 +314,10 @@ int oracle_quant_qk(const uint16_t* x, int B, int S, int H, int D, float mult, i
         for (int i = i0; i < i1; ++i)
           for (int d = 0; d < D; ++d) {
             const float y = bf16_to_f32(x[idx_bshd(b, i, h, d, S, H, D)]) * mult;
-            if (!isfinite(y)) return ORACLE_ENONFINITE;
+            if (!isfinite(y)) {
+#pragma omp atomic write
+              status = ORACLE_ENONFINITE;
+            }
             const float ay = fabsf(y);
             if (ay > amax) amax = ay;
           }
@@ -315,7 +336,7 @@ int oracle_quant_qk(const uint16_t* x, int B, int S, int H, int D, float mult, i
             codes[(((int64_t)b * H + h) * S_pad + i) * D + d] = code;
           }
       }
-  return ORACLE_OK;
+  return status;
 }
 
 /*
@@ -329,13 +350,20 @@ int oracle_quant_qk(const uint16_t* x, int B, int S, int H, int D, float mult, i
 int oracle_quant_v(const uint16_t* v, int B, int S, int H, int D, int S_pad, uint8_t* codes,
                    float* scales) {
   if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || S_pad < S) return ORACLE_EINVAL;
+  int status = ORACLE_OK;
+  e4m3_fill();
+  /* channels are independent; spread them over the host cores */
+#pragma omp parallel for collapse(3) schedule(static)
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < H; ++h)
       for (int ch = 0; ch < D; ++ch) {
         float amax = 0.0f;
         for (int j = 0; j < S; ++j) {
           const float y = bf16_to_f32(v[idx_bshd(b, j, h, ch, S, H, D)]);
-          if (!isfinite(y)) return ORACLE_ENONFINITE;
+          if (!isfinite(y)) {
+#pragma omp atomic write
+            status = ORACLE_ENONFINITE;
+          }
           if (fabsf(y) > amax) amax = fabsf(y);
         }
         const float sv = amax / 448.0f;
@@ -347,5 +375,5 @@ int oracle_quant_v(const uint16_t* v, int B, int S, int H, int D, int S_pad, uin
           row[j] = code;
         }
       }
-  return ORACLE_OK;
+  return status;
 }

@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Gates (from the DiT attention workloads' acceptance criteria):
+  * BF16 attention: max |gpu - exact| <= 1e-2 and cosine >= 0.99999 against
+    exact fp64 attention on the same BF16 inputs.
+  * Sage prepare: INT8 Q/K codes, FP32 scales, FP8 V codes and V scales
+    bit-exact against the scalar fp32 quantizer, over the full tensors.
+  * Sage attention: cosine >= 0.998 and relative L2 <= 5e-2 against exact fp64
+    attention on the original BF16 inputs.
+Small shapes check every output row; the DiT-sized workloads check a seeded
+sample of 4096 query rows that always includes the last 32 rows of the first
+and last head (the ragged query tail); every row crosses the ragged key tail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import image_dit_amd as ia
+import oracle
+from image_dit_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS = 1e-2
+BF16_MIN_COS = 0.99999
+SAGE_MIN_COS = 0.998
+SAGE_MAX_REL_L2 = 5e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def metrics(got, ref):
+    got = np.asarray(got, dtype=np.float64).reshape(-1, ref.shape[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(-1, ref.shape[-1])
+    cos = float(np.sum(got * ref) / (np.linalg.norm(got) * np.linalg.norm(ref)))
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    row_cos = np.sum(got * ref, axis=1) / (np.linalg.norm(got, axis=1) * np.linalg.norm(ref, axis=1))
+    return dict(cos=cos, rel_l2=rel, max_abs=float(np.max(np.abs(got - ref))),
+                min_row_cos=float(np.min(row_cos)), median_row_cos=float(np.median(row_cos)))
+
+
+def gather_rows(out_gpu, rows):
+    """Rows (b, h, i) of a [B, S, H, D] GPU tensor, as fp64 numpy."""
+    idx = torch.from_numpy(rows).to(out_gpu.device)
+    sel = out_gpu[idx[:, 0], idx[:, 2], idx[:, 1]]
+    return sel.float().cpu().numpy().astype(np.float64)
+
+
+class Case:
+    def __init__(self, w: synth.Workload):
+        self.w = w
+        log("[case %s] generating B=%d H=%d S=%d seed=%d" % (w.name, w.B, w.H, w.S, w.seed))
+        self.q, self.k, self.v = synth.workload_qkv(w)
+        self.rows = synth.sample_rows(w.B, w.S, w.H, n=4096, seed=w.seed + 1)
+        log("[case %s] oracle: exact attention on %d rows" % (w.name, len(self.rows)))
+        self.ref = oracle.attn_rows(self.q, self.k, self.v, w.scale, rows=self.rows)
+        self._prep = None
+        dev = torch.device("cuda", 0)
+        self.qd, self.kd, self.vd = (t.to(dev) for t in (self.q, self.k, self.v))
+
+    @property
+    def prep_ref(self):
+        if self._prep is None:
+            log("[case %s] oracle: prepare quantizer" % self.w.name)
+            self._prep = oracle.sage_prepare(self.q, self.k, self.v, self.w.scale)
+        return self._prep
+
+
+@pytest.fixture(scope="module", params=list(synth.WORKLOADS))
+def case(request):
+    c = Case(synth.WORKLOADS[request.param])
+    yield c
+    del c
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_bf16_attention_matches_oracle(case):
+    w = case.w
+    log("[bf16 %s] attn_fwd_bf16" % w.name)
+    out = ia.attn_fwd_bf16(case.qd, case.kd, case.vd, w.scale)
+    torch.cuda.synchronize()
+    got = gather_rows(out, case.rows)
+    mt = metrics(got, case.ref)
+    log("[bf16 %s] %s" % (w.name, mt))
+    assert np.all(np.isfinite(got))
+    assert mt["max_abs"] <= BF16_MAX_ABS, mt
+    assert mt["cos"] >= BF16_MIN_COS, mt
+
+
+@pytest.mark.timeout(600)
+def test_sage_prepare_bit_exact(case):
+    w = case.w
+    log("[prep %s] sage_prepare" % w.name)
+    got = ia.sage_prepare(case.qd, case.kd, case.vd, w.scale)
+    torch.cuda.synchronize()
+    names = ("q_i8", "q_scale", "k_i8", "k_scale", "v_fp8", "v_scale")
+    for name, g, r in zip(names, got, case.prep_ref):
+        g = g.cpu().numpy()
+        assert g.shape == r.shape, (name, g.shape, r.shape)
+        if g.dtype == np.float32:
+            bad = np.count_nonzero(g.view(np.uint32) != r.view(np.uint32))
+        else:
+            bad = np.count_nonzero(g != r)
+        log("[prep %s] %s: %d of %d differ" % (w.name, name, bad, g.size))
+        assert bad == 0, name
+
+
+@pytest.mark.timeout(600)
+def test_sage_attention_matches_oracle(case):
+    w = case.w
+    log("[sage %s] sage_prepare + sage_attn_fwd" % w.name)
+    out = ia.sage_attention(case.qd, case.kd, case.vd, w.scale)
+    torch.cuda.synchronize()
+    got = gather_rows(out, case.rows)
+    mt = metrics(got, case.ref)
+    log("[sage %s] %s" % (w.name, mt))
+    assert np.all(np.isfinite(got))
+    assert mt["cos"] >= SAGE_MIN_COS, mt
+    assert mt["rel_l2"] <= SAGE_MAX_REL_L2, mt
+
+
+# ---------------------------------------------------------------- edge shapes
+
+RAGGED = [(1, 1, 1), (1, 31, 2), (2, 33, 3), (1, 63, 1), (1, 65, 2), (1, 127, 1), (1, 129, 2),
+          (2, 255, 1), (1, 257, 2), (1, 1000, 2), (3, 300, 5)]
+
+
+@pytest.mark.parametrize("B,S,H", RAGGED)
+def test_ragged_shapes_every_row(B, S, H):
+    scale = float(np.float32(1 / math.sqrt(128)))
+    q, k, v = synth.make_qkv(B, S, H, seed=100 + S + 7 * H + B)
+    log("[ragged B=%d S=%d H=%d]" % (B, S, H))
+    ref = oracle.attn_rows(q, k, v, scale)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = ia.attn_fwd_bf16(qd, kd, vd, scale).float().cpu().numpy()
+    mt = metrics(out, ref)
+    log("[ragged bf16] %s" % mt)
+    assert mt["max_abs"] <= BF16_MAX_ABS and mt["cos"] >= BF16_MIN_COS, mt
+    prep = ia.sage_prepare(qd, kd, vd, scale)
+    for name, g, r in zip(("q_i8", "q_scale", "k_i8", "k_scale", "v_fp8", "v_scale"), prep,
+                          oracle.sage_prepare(q, k, v, scale)):
+        g = g.cpu().numpy()
+        same = np.array_equal(g.view(np.uint32), r.view(np.uint32)) if g.dtype == np.float32 else np.array_equal(g, r)
+        assert same, name
+    sout = ia.sage_attn_fwd(prep, S, H, scale).float().cpu().numpy()
+    ms = metrics(sout, ref)
+    log("[ragged sage] %s" % ms)
+    assert ms["cos"] >= SAGE_MIN_COS and ms["rel_l2"] <= SAGE_MAX_REL_L2, ms
+
+
+def test_single_key_returns_v_exactly():
+    # S = 1: softmax is 1, O = V (BF16 path exact; Sage path within its gate)
+    q, k, v = synth.make_qkv(2, 1, 4, seed=5)
+    dev = torch.device("cuda", 0)
+    out = ia.attn_fwd_bf16(q.to(dev), k.to(dev), v.to(dev), 0.0883883).cpu()
+    assert torch.equal(out, v)
+
+
+def test_non_default_stream_and_determinism():
+    w = synth.WORKLOADS["tiny"]
+    q, k, v = (t.cuda() for t in synth.make_qkv(2, 1111, 3, seed=77))
+    ref = ia.attn_fwd_bf16(q, k, v, w.scale)
+    sref = ia.sage_attention(q, k, v, w.scale)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            a = ia.attn_fwd_bf16(q, k, v, w.scale, stream=s)
+            b = ia.sage_attention(q, k, v, w.scale, stream=s)
+    s.synchronize()
+    assert torch.equal(a, ref), "BF16 path is not run-to-run bitwise deterministic"
+    assert torch.equal(b, sref), "Sage path is not run-to-run bitwise deterministic"
+
+
+def test_kv_token_reversal_is_a_noop():
+    # reversing K/V token order together leaves attention unchanged up to the
+    # order of the fp32 sums
+    scale = float(np.float32(1 / math.sqrt(128)))
+    q, k, v = (t.cuda() for t in synth.make_qkv(1, 2000, 4, seed=78))
+    rev = torch.arange(1999, -1, -1, device="cuda")
+    a = ia.attn_fwd_bf16(q, k, v, scale).float()
+    b = ia.attn_fwd_bf16(q, k[:, rev].contiguous(), v[:, rev].contiguous(), scale).float()
+    assert (a - b).abs().max().item() <= BF16_MAX_ABS
+
+
+def test_outputs_untouched_on_argument_error():
+    q, k, v = (t.cuda() for t in synth.make_qkv(1, 64, 2, seed=79))
+    out = torch.full_like(q, 3.0)
+    with pytest.raises(ia.DitAttnError):
+        ia.attn_fwd_bf16(q, k, v, -1.0, out=out)
+    torch.cuda.synchronize()
+    assert bool((out.float() == 3.0).all())
