@@ -32,17 +32,19 @@ def compile_flags():
             "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
+def build(force: bool = True, verbose: bool = False, out_path: str = None, defines=()) -> str:
+    """Compile every source and link libditattn.so (or `out_path`, with extra -D defines)."""
+    lib_path = out_path or LIB
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     deps = srcs + [os.path.join(CSRC, "common.hpp"), os.path.join(CSRC, "launch.hpp"),
                    os.path.join(ROOT, "include", "ditattn.h")]
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(os.path.getmtime(d) for d in deps):
-        return LIB
+    if not force and os.path.exists(lib_path) and os.path.getmtime(lib_path) >= max(os.path.getmtime(d) for d in deps):
+        return lib_path
     with tempfile.TemporaryDirectory(prefix="ditattn_build_") as tmp:
         objs = []
         for src in srcs:
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [hipcc()] + compile_flags() + ["-c", src, "-o", obj]
+            cmd = [hipcc()] + compile_flags() + ["-D" + d for d in defines] + ["-c", src, "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError("hipcc failed on %s:\n%s" % (src, r.stderr))
@@ -54,9 +56,9 @@ def build(force: bool = True, verbose: bool = False) -> str:
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n%s" % r.stderr)
-        shutil.copyfile(out, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
-    return LIB
+        shutil.copyfile(out, lib_path + ".tmp")
+        os.replace(lib_path + ".tmp", lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

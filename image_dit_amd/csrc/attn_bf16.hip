@@ -34,28 +34,38 @@
 //     math: every p and l use the same stale max, which cancels in acc / l.
 //   * Ragged tail: key rows >= S are zero-filled in LDS and their scores set to
 //     -inf; query rows >= S are computed on zeros and not stored.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ditattn {
 namespace bf16attn {
+
+// Tuning knobs (compile-time; defaults are the measured choice).
+#ifndef DITATTN_BF16_OCC
+#define DITATTN_BF16_OCC 2  // workgroups per CU the register budget is sized for
+#endif
+#ifndef DITATTN_BF16_QG
+#define DITATTN_BF16_QG 1   // 32-row query groups per wave
+#endif
 
 constexpr int BK = 64;      // keys per K/V tile
 constexpr int NW = 4;       // waves per workgroup
 constexpr int ROW_CHUNKS = 16;  // 16-byte chunks per 128-channel BF16 row
 constexpr float kLazyThresh = 8.0f;
 
-// chunk index (16 B units) of (row, chunk) inside a K or V tile
-__device__ __forceinline__ int k_chunk(int row, int c) { return row * ROW_CHUNKS + (c ^ (row & 15)); }
-__device__ __forceinline__ int v_chunk(int row, int c) { return row * ROW_CHUNKS + (c ^ ((row & 3) << 2)); }
+
+// Byte layout of the LDS ring: [buf][K | V][64 rows x 256 B].
+constexpr int TILE_BYTES = BK * 256;
+constexpr int BUF_BYTES = 2 * TILE_BYTES;
 
 template <int QG>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64, DITATTN_BF16_OCC)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o, int S, int H, float c,
                      int num_qt, int n_tiles) {
   constexpr int BQ = NW * QG * 32;
-  __shared__ __attribute__((aligned(16))) uint4 lds_k[2][BK * ROW_CHUNKS];
-  __shared__ __attribute__((aligned(16))) uint4 lds_v[2][BK * ROW_CHUNKS];
+  __shared__ __attribute__((aligned(16))) char lds[2 * BUF_BYTES];
 
   const int L = xcd_remap(blockIdx.x, n_tiles);
   const int bh = L / num_qt;
@@ -64,10 +74,11 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int tid = threadIdx.x;
   const int wave = tid >> 6, l = tid & 63, hl = l >> 5, ln = l & 31;
   const int64_t tok = (int64_t)H * kHeadDim;  // elements between consecutive tokens
+  const uint32_t tok_bytes = (uint32_t)(tok * 2);
   const int64_t base = ((int64_t)b * S * H + h) * kHeadDim;
   const __bf16* qbh = q + base;
-  const __bf16* kbh = k + base;
-  const __bf16* vbh = v + base;
+  const char* kbh = (const char*)(k + base);
+  const char* vbh = (const char*)(v + base);
   __bf16* obh = o + base;
 
   // Q^T operand, resident for the whole key loop: Q[q0 + 32 g + ln][16 ks + 8 hl + 0..7].
@@ -93,40 +104,54 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int dt = 0; dt < 4; ++dt) acc[g][dt] = f32x16{};
   }
 
-  // Staging: thread tid moves chunk (tid & 15) of rows (tid >> 4) + 16 p, p = 0..3.
-  const int st_row = tid >> 4, st_chunk = tid & 15;
-  uint4 kst[4], vst[4];
-  auto load_tile = [&](int t) {
+  // ---- global -> LDS (direct).  Wave w, instruction n writes LDS rows 16 w + 4 n + l / 16,
+  // physical chunk l % 16; the lane fetches the logical chunk that lands there.
+  const int p_chunk = l & 15;
+  auto issue_tile = [&](int t, int buf, bool clamp) {
+    const int j0 = t * BK;
+    const char* kt = kbh + (int64_t)j0 * tok * 2;
+    const char* vt = vbh + (int64_t)j0 * tok * 2;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int j = t * BK + st_row + 16 * p;
-      if (j < S) {
-        kst[p] = *(const uint4*)(kbh + j * tok + 8 * st_chunk);
-        vst[p] = *(const uint4*)(vbh + j * tok + 8 * st_chunk);
-      } else {
-        kst[p] = uint4{0, 0, 0, 0};
-        vst[p] = uint4{0, 0, 0, 0};
-      }
+    for (int n = 0; n < 4; ++n) {
+      const int r = 16 * wave + 4 * n + (l >> 4);
+      int rr = r;
+      if (clamp && j0 + r >= S) rr = S - 1 - j0;  // rows past the end repeat the last real key
+      const uint32_t koff = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ (r & 15));
+      const uint32_t voff = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ ((r & 3) << 2));
+      char* kdst = lds + buf * BUF_BYTES + (16 * wave + 4 * n) * 256;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + koff),
+                                       (DITATTN_LDS void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + voff),
+                                       (DITATTN_LDS void*)(kdst + TILE_BYTES), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+
+  // ---- per-lane LDS read offsets (bytes, relative to the tile), constant over the loop
+  // K (A operand of S^T): row 32 tt + ln, logical chunk 2 ks + hl, physical chunk ^ (row & 15).
+  uint32_t kofs[8];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      lds_k[buf][k_chunk(st_row + 16 * p, st_chunk)] = kst[p];
-      lds_v[buf][v_chunk(st_row + 16 * p, st_chunk)] = vst[p];
+  for (int ks = 0; ks < 8; ++ks) kofs[ks] = ln * 256 + 16 * ((2 * ks + hl) ^ (ln & 15));
+  // V (A operand of O^T, transposed read): lane j of its 16-lane group addresses
+  // row 16 cc + 8 E + 4 hl + j / 4, columns 32 dt + 16 (group & 1) + 4 (j & 3) .. + 3.
+  uint32_t vofs[4];
+  {
+    const int grp = l >> 4, j = l & 15, qrow = j >> 2;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int col = 32 * dt + 16 * (grp & 1) + 4 * (j & 3);
+      vofs[dt] = (4 * hl + qrow) * 256 + 16 * ((col >> 3) ^ (qrow << 2)) + (col & 7) * 2;
     }
-  };
+  }
 
   const int n_kt = (S + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
 
-  for (int t = 0; t < n_kt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_kt) load_tile(t + 1);
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](auto buf_c, auto tail_c, int t) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr bool tail = decltype(tail_c)::value;
+    const char* kb = lds + buf * BUF_BYTES;
+    const char* vb = kb + TILE_BYTES;
 
-    // ---- S^T = K Q^T for 64 keys x 32 QG queries
     f32x16 s[2][QG];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -136,15 +161,13 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_k[buf][k_chunk(32 * tt + ln, 2 * ks + hl)]);
+        const bf16x8 kf = *(const DITATTN_LDS bf16x8*)((const DITATTN_LDS char*)kb + kofs[ks] + tt * 32 * 256);
 #pragma unroll
         for (int g = 0; g < QG; ++g) s[tt][g] = mfma_bf16_32x32x16(kf, qf[g][ks], s[tt][g]);
       }
     }
-
-    // ---- mask keys >= S (only the last, partial tile)
-    const int j0 = t * BK;
-    if (j0 + BK > S) {
+    if constexpr (tail) {
+      const int j0 = t * BK;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -156,15 +179,12 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
     }
 
-    // ---- online softmax (base 2), P -> BF16 B operands
     bf16x8 pf[QG][4];
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
-      float mx = s[0][g][0];
+      float mx = fmaxf(s[0][g][0], s[1][g][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][g][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][g][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][g][r], s[1][g][r]));
       mx = half_pair_max(mx) * c;
       // raise the running max only when it grew by more than the threshold
       if (__builtin_amdgcn_ballot_w64(mx > m[g] + kLazyThresh) != 0) {
@@ -196,22 +216,15 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       lsum[g] += ps;
     }
 
-    // ---- O^T += V^T P^T
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        // lane l, element e of A = V[16 cc + 8 (e / 4) + 4 hl + e % 4][32 dt + ln]
-        const int grp = l >> 4, j = l & 15;
-        const int col = 32 * dt + 16 * (grp & 1) + 4 * (j & 3);  // BF16 column
         i16x4 part[2];
 #pragma unroll
-        for (int E = 0; E < 2; ++E) {
-          const int row = 16 * cc + 8 * E + 4 * hl + (j >> 2);
-          const int byte = v_chunk(row, col >> 3) * 16 + (col & 7) * 2;
+        for (int E = 0; E < 2; ++E)
           part[E] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DITATTN_LDS i16x4*)((DITATTN_LDS char*)&lds_v[buf][0] + byte));
-        }
+              (DITATTN_LDS i16x4*)((DITATTN_LDS char*)vb + vofs[dt] + (16 * cc + 8 * E) * 256));
         // whole-vector casts only: element-wise bf16 <-> i16 bit casts are not
         // lowered reliably by this compiler
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -219,9 +232,40 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         for (int g = 0; g < QG; ++g) acc[g][dt] = mfma_bf16_32x32x16(va, pf[g][cc], acc[g][dt]);
       }
     }
+  };
 
-    if (t + 1 < n_kt) store_tile(buf ^ 1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using Full = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+  const bool ragged = (S % BK) != 0;
+  const int n_full = ragged ? n_kt - 1 : n_kt;  // tiles with 64 real keys
+
+  issue_tile(0, 0, n_full == 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile loads have landed in LDS
+  __syncthreads();
+  int t = 0;
+  // full tiles, two per trip so the buffer offsets are immediates
+  for (; t + 1 < n_full; t += 2) {
+    issue_tile(t + 1, 1, false);
+    tile(I0{}, Full{}, t);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (t + 2 < n_kt) issue_tile(t + 2, 0, t + 2 >= n_full);
+    tile(I1{}, Full{}, t + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (t < n_full) {  // one full tile left, in buffer 0 (t is even)
+    if (t + 1 < n_kt) issue_tile(t + 1, 1, true);
+    tile(I0{}, Full{}, t);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    ++t;
+  }
+  if (t < n_kt) {  // the ragged tail tile, in buffer t & 1
+    if (t & 1) tile(I1{}, Tail{}, t);
+    else tile(I0{}, Tail{}, t);
   }
 
   // ---- epilogue: O = acc / l, BF16, rows < S
@@ -247,7 +291,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 }  // namespace bf16attn
 
 // Query rows per workgroup of the launched configuration.
-constexpr int kBf16QG = 1;
+constexpr int kBf16QG = DITATTN_BF16_QG;
 constexpr int kBf16BQ = bf16attn::NW * kBf16QG * 32;
 
 int bf16_tile_rows() { return kBf16BQ; }
