@@ -184,7 +184,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int g = 0; g < QG; ++g) {
       float mx = fmaxf(s[0][g][0], s[1][g][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][g][r], s[1][g][r]));
+      for (int r = 1; r < 16; ++r) mx = max3(mx, s[0][g][r], s[1][g][r]);
       mx = half_pair_max(mx) * c;
       // raise the running max only when it grew by more than the threshold
       if (__builtin_amdgcn_ballot_w64(mx > m[g] + kLazyThresh) != 0) {
@@ -196,42 +196,43 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         for (int dt = 0; dt < 4; ++dt) acc[g][dt] *= alpha;
       }
       const float mneg = -m[g];
-      float ps = 0.0f;
+      float p[32];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float p[8];
+        for (int r = 0; r < 16; ++r) p[16 * tt + r] = fast_exp2(fmaf(s[tt][g][r], c, mneg));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(fmaf(s[tt][g][8 * half + e], c, mneg));
-            ps += p[e];
-          }
-          bf16x8 pv;
+      for (int cc = 0; cc < 4; ++cc) {
+        bf16x8 pv;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = (__bf16)p[e];
-          pf[g][2 * tt + half] = pv;
-        }
+        for (int e = 0; e < 8; ++e) pv[e] = (__bf16)p[8 * cc + e];
+        pf[g][cc] = pv;
       }
-      lsum[g] += ps;
+      lsum[g] += tree_sum<32>(p);
     }
 
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    // V^T fragments for one 16-key chunk: 4 channel tiles x 2 transposed reads
+    const uint32_t vaddr = (uint32_t)(uintptr_t)(const DITATTN_LDS char*)vb;
+    auto pv_chunk = [&](auto cc_c) {
+      constexpr int cc = decltype(cc_c)::value;
+      u32x2 r[4][2];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        i16x4 part[2];
+        r[dt][0] = ds_read_tr16_b64<(16 * cc) * 256>(vaddr + vofs[dt]);
+        r[dt][1] = ds_read_tr16_b64<(16 * cc + 8) * 256>(vaddr + vofs[dt]);
+      }
+      lds_wait(r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]);
 #pragma unroll
-        for (int E = 0; E < 2; ++E)
-          part[E] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DITATTN_LDS i16x4*)((DITATTN_LDS char*)vb + vofs[dt] + (16 * cc + 8 * E) * 256));
-        // whole-vector casts only: element-wise bf16 <-> i16 bit casts are not
-        // lowered reliably by this compiler
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{r[dt][0][0], r[dt][0][1], r[dt][1][0], r[dt][1][1]});
 #pragma unroll
         for (int g = 0; g < QG; ++g) acc[g][dt] = mfma_bf16_32x32x16(va, pf[g][cc], acc[g][dt]);
       }
-    }
+    };
+    pv_chunk(std::integral_constant<int, 0>{});
+    pv_chunk(std::integral_constant<int, 1>{});
+    pv_chunk(std::integral_constant<int, 2>{});
+    pv_chunk(std::integral_constant<int, 3>{});
   };
 
   using I0 = std::integral_constant<int, 0>;

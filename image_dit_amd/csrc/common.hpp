@@ -55,6 +55,42 @@ __device__ __forceinline__ float half_pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b, c) in one v_max3_f32.  fmaxf on MFMA results makes the compiler
+// canonicalize every operand first (one extra v_max per value); the scores
+// here are never signalling NaNs, so the plain instruction is exact.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Sum of n values as a balanced tree (independent adds instead of one chain).
+template <int N>
+__device__ __forceinline__ float tree_sum(const float* x) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else {
+    return tree_sum<N / 2>(x) + tree_sum<N - N / 2>(x + N / 2);
+  }
+}
+
+// ds_read_b64_tr_b16 issued as inline assembly, so the compiler does not
+// treat it as aliasing in-flight global->LDS copies of the OTHER buffer and
+// insert a vmcnt(0) before it.  The caller must run lds_wait() on the
+// results before using them.  `addr` is an LDS byte address.
+template <int OFFSET>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET) : "memory");
+  return r;
+}
+// Wait for every outstanding LDS read and make the given registers depend on
+// the wait, so no consumer can be scheduled above it.
+__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d, u32x2& e,
+                                         u32x2& f, u32x2& g, u32x2& h) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+}
+
 // Round two fp32 values to BF16 (nearest even) and pack them, low half first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
