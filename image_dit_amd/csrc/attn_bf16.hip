@@ -144,11 +144,15 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   const int n_kt = (S + BK - 1) / BK;
+  const bool ragged = (S % BK) != 0;
 
   // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](auto buf_c, auto tail_c, int t) {
-    constexpr int buf = decltype(buf_c)::value;
+  // One key tile from LDS buffer `buf` (a constant in the main loop, a runtime
+  // value for the last tile, which always goes through one code path so that
+  // nothing is merged between its last MFMA and the epilogue).
+  auto tile = [&](auto buf_v, auto tail_c, int t) {
     constexpr bool tail = decltype(tail_c)::value;
+    const int buf = buf_v;
     const char* kb = lds + buf * BUF_BYTES;
     const char* vb = kb + TILE_BYTES;
 
@@ -167,16 +171,18 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
     }
     if constexpr (tail) {
-      const int j0 = t * BK;
+      if (ragged) {
+        const int j0 = t * BK;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 32 * tt + 8 * (r >> 2) + 4 * hl + (r & 3);
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 32 * tt + 8 * (r >> 2) + 4 * hl + (r & 3);
 #pragma unroll
-          for (int g = 0; g < QG; ++g)
-            if (j >= S) s[tt][g][r] = -INFINITY;
-        }
+            for (int g = 0; g < QG; ++g)
+              if (j >= S) s[tt][g][r] = -INFINITY;
+          }
+      }
     }
 
     bf16x8 pf[QG][4];
@@ -221,7 +227,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         r[dt][0] = ds_read_tr16_b64<(16 * cc) * 256>(vaddr + vofs[dt]);
         r[dt][1] = ds_read_tr16_b64<(16 * cc + 8) * 256>(vaddr + vofs[dt]);
       }
-      lds_wait(r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]);
+      lds_wait<0>(r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{r[dt][0][0], r[dt][0][1], r[dt][1][0], r[dt][1][1]});
@@ -238,38 +244,36 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using Full = std::integral_constant<bool, false>;
-  using Tail = std::integral_constant<bool, true>;
-  const bool ragged = (S % BK) != 0;
-  const int n_full = ragged ? n_kt - 1 : n_kt;  // tiles with 64 real keys
+  using Last = std::integral_constant<bool, true>;
+  const int n_main = n_kt - 1;  // tiles before the last one
 
-  issue_tile(0, 0, n_full == 0);
+  issue_tile(0, 0, n_kt == 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile loads have landed in LDS
   __syncthreads();
   int t = 0;
-  // full tiles, two per trip so the buffer offsets are immediates
-  for (; t + 1 < n_full; t += 2) {
+  // two tiles per trip so the buffer offsets are immediates
+  for (; t + 1 < n_main; t += 2) {
     issue_tile(t + 1, 1, false);
     tile(I0{}, Full{}, t);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 2 < n_kt) issue_tile(t + 2, 0, t + 2 >= n_full);
+    issue_tile(t + 2, 0, t + 2 == n_kt - 1);
     tile(I1{}, Full{}, t + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  if (t < n_full) {  // one full tile left, in buffer 0 (t is even)
-    if (t + 1 < n_kt) issue_tile(t + 1, 1, true);
+  if (t < n_main) {  // one more tile before the last, in buffer 0 (t is even)
+    issue_tile(t + 1, 1, true);
     tile(I0{}, Full{}, t);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     ++t;
   }
-  if (t < n_kt) {  // the ragged tail tile, in buffer t & 1
-    if (t & 1) tile(I1{}, Tail{}, t);
-    else tile(I0{}, Tail{}, t);
-  }
+  tile(t & 1, Last{}, t);  // the last tile (masked when S is ragged)
 
   // ---- epilogue: O = acc / l, BF16, rows < S
+#pragma unroll
+  for (int g = 0; g < QG; ++g) mfma_drain(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     const float inv = 1.0f / half_pair_sum(lsum[g]);

@@ -10,60 +10,74 @@
 //
 // gfx950 mapping
 //   * Workgroup = 4 waves x 32 query rows (BQ = 128) of one (b, h); XCD-aware
-//     tile order as in the BF16 kernel.  Key tiles of BK = 64.
+//     tile order as in the BF16 kernel; two workgroups per CU.  Key tiles of
+//     BK = 64, double-buffered, copied global -> LDS directly.
 //   * S^T = K Q^T on v_mfma_i32_32x32x32_i8 (exact int32; |acc| <= 128 * 127^2
 //     < 2^24 so the conversion to fp32 is exact).  Q codes stay in registers.
-//     Scores in log2 units: x = acc * q_scale[query block] * k_scale[key block];
-//     both scales are uniform over a 32 x 32 sub-tile (a query group is one
-//     32-row block, a key sub-tile is one 32-row block).
-//   * Key rows feed the A operand with bits 2 and 3 of the row index swapped,
-//     so accumulator registers 0..7 of a lane hold 8 consecutive keys and
-//     registers 8..15 another 8: P's B operand for the FP8 MFMA is then read
-//     from V^T in runs of 8 bytes.
+//     Scores in log2 units: x = acc * q_scale[query block] * k_scale[key block].
+//   * Key rows are fed to the A operand in an order that gives every half-wave
+//     32 consecutive keys of the tile (one 32-row K block, hence one k_scale):
+//     P's FP8 B operand of a lane is then 32 consecutive keys, and the matching
+//     V^T operand is two 16-byte LDS reads.
 //   * P V on v_mfma_scale_f32_32x32x64_f8f6f4 (both operands e4m3, unit block
 //     scales): A = V^T tile (channels x 64 keys) in LDS, B = P from registers.
-//   * P is stored as p * 2^8 in e4m3: exp2(x - m + 8) gives it directly (p <= 1
-//     since the running max is exact, so p * 2^8 <= 256 < 448; values down to
-//     2^-14 stay normal).  The row sum l accumulates the same fp32 values, so
-//     O = acc * v_scale / l needs no extra factor.
-//   * Keys j >= S (zero codes, which would score 0) are masked to -inf.
+//   * P is stored as p * 2^8 in e4m3: exp2(x - m + 8) gives it directly.  The
+//     running max is raised lazily (threshold 0.8 in log2 units), so p <= 2^0.8
+//     and p * 2^8 <= 445.7 < 448; values down to 2^-14 stay normal.  The row
+//     sum l accumulates the same fp32 values, so O = acc * v_scale / l.
+//   * Keys j >= S (zero codes, which would score 0) are masked to -inf in the
+//     last tile only.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ditattn {
 namespace sageattn {
 
+#ifndef DITATTN_SAGE_OCC
+#define DITATTN_SAGE_OCC 2  // workgroups per CU the register budget is sized for
+#endif
+
 constexpr int BK = 64;
 constexpr int NW = 4;
 constexpr int BQ = NW * 32;
 constexpr float kPScaleLog2 = 8.0f;  // P is stored as p * 2^8
+// The running max is raised only when a row's tile max exceeds it by more than
+// this (log2 units).  P then stays <= 2^0.8, so p * 2^8 <= 445.7 still fits
+// e4m3 (max 448).
+constexpr float kLazyThresh = 0.8f;
 
-// K tile: 64 rows x 128 B (8 chunks of 16 B), chunk XOR-swizzled by (row >> 1) & 7.
-__device__ __forceinline__ int k_chunk(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
-// V^T tile: 128 channel rows x 64 B (8 units of 8 B), unit XOR-swizzled by (row >> 2) & 7.
-__device__ __forceinline__ int v_unit(int row, int u) { return row * 8 + (u ^ ((row >> 2) & 7)); }
-// Accumulator row m -> key row fed to the MFMA (bits 2 and 3 swapped; an involution).
-__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// LDS tiles (bytes):  K: 64 key rows x 128 B, 16-B chunk c of row r stored at c ^ ((r >> 1) & 7).
+//                     V^T: 128 channel rows x 64 B, chunk c of row r at c ^ ((r >> 2) & 3).
+constexpr int KT_BYTES = BK * 128;
+constexpr int VT_BYTES = 128 * BK;
+constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
 
-__global__ void __launch_bounds__(NW * 64)
+// Accumulator row m of sub-tile tt holds key 32 * ((m >> 2) & 1) + 16 tt + 4 (m >> 3) + (m & 3)
+// of the 64-key tile.  Then register r of a lane in half hl holds key 32 hl + 16 tt + r: P's
+// 32 FP8 bytes of a lane are 32 consecutive keys and V^T is read with two 16-byte loads.
+__device__ __forceinline__ int key_of_row(int m, int tt) { return 32 * ((m >> 2) & 1) + 16 * tt + 4 * (m >> 3) + (m & 3); }
+
+__global__ void __launch_bounds__(NW * 64, DITATTN_SAGE_OCC)
 sage_attn_fwd_kernel(const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
                      const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
                      const uint8_t* __restrict__ v_fp8, const float* __restrict__ v_scale,
                      __bf16* __restrict__ o, int S, int H, int S_pad, int num_qt, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint4 lds_k[2][BK * 8];    // 2 x 8 KB
-  __shared__ __attribute__((aligned(16))) uint2 lds_v[2][128 * 8];   // 2 x 8 KB
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE_BYTES];  // 32 KB
 
   const int L = xcd_remap(blockIdx.x, n_tiles);
   const int bh = L / num_qt;
   const int qt = L - bh * num_qt;
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, l = tid & 63, hl = l >> 5, ln = l & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, hl = l >> 5, ln = l & 31;
   const int nblk = S_pad / 32;
 
   const int8_t* qbh = q_i8 + (int64_t)bh * S_pad * kHeadDim;
-  const int8_t* kbh = k_i8 + (int64_t)bh * S_pad * kHeadDim;
-  const uint8_t* vbh = v_fp8 + (int64_t)bh * kHeadDim * S_pad;
+  const char* kbh = (const char*)(k_i8 + (int64_t)bh * S_pad * kHeadDim);
+  const char* vbh = (const char*)(v_fp8 + (int64_t)bh * kHeadDim * S_pad);
   const float* ksc = k_scale + (int64_t)bh * nblk;
 
   // Q codes (B operand), resident: Q[q0 + ln][32 ks + 16 hl + 0..15].  Rows < S_pad always.
@@ -77,38 +91,58 @@ sage_attn_fwd_kernel(const int8_t* __restrict__ q_i8, const float* __restrict__ 
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
   float m = -INFINITY, lsum = 0.0f;
+  const int unit_scale = unit_e8m0_scale();
 
-  // staging: K tile = 8 KB contiguous (2 x 16 B per thread); V^T tile = 128 rows x 64 B.
-  uint4 kst[2], vst[2];
-  auto load_tile = [&](int t) {
+  // ---- global -> LDS (direct); every lane fetches the chunk that lands in its LDS slot.
+  // K: instruction n of wave w fills LDS rows 8 (2 w + n) .. + 7 (1 KB), lane -> row + l / 8, slot l % 8.
+  // V^T: instruction n of wave w fills channel rows 16 (2 w + n) .. + 15, lane -> row + l / 4, slot l % 4.
+  uint32_t kgo[2], vgo[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int kr = 8 * (2 * wave + n) + (l >> 3), kc = (l & 7) ^ ((kr >> 1) & 7);
+    kgo[n] = kr * 128 + 16 * kc;
+    const int vr = 16 * (2 * wave + n) + (l >> 2), vc = (l & 3) ^ ((vr >> 2) & 3);
+    vgo[n] = vr * S_pad + 16 * vc;
+  }
+  auto issue = [&](int t, int stage) {
     const int j0 = t * BK;
+    const char* kt = kbh + (int64_t)j0 * kHeadDim;
+    const char* vt = vbh + j0;
+    char* dst = lds + stage * STAGE_BYTES;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int idx = tid + 256 * p;  // 0..511
-      kst[p] = *(const uint4*)(kbh + (int64_t)j0 * kHeadDim + 16 * idx);
-      const int row = idx >> 2, c16 = idx & 3;
-      vst[p] = *(const uint4*)(vbh + (int64_t)row * S_pad + j0 + 16 * c16);
+    for (int n = 0; n < 2; ++n) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + kgo[n]),
+                                       (DITATTN_LDS void*)(dst + (2 * wave + n) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + vgo[n]),
+                                       (DITATTN_LDS void*)(dst + KT_BYTES + (2 * wave + n) * 1024), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
+
+  // ---- per-lane LDS read offsets
+  // K (A operand): row key_of_row(ln, tt) (tt = 1 adds 16 rows, same swizzle), logical chunk 2 ks + hl.
+  uint32_t kofs[4];
+  {
+    const int row = key_of_row(ln, 0);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int idx = tid + 256 * p;
-      lds_k[buf][k_chunk(idx >> 3, idx & 7)] = kst[p];
-      const int row = idx >> 2, c16 = idx & 3;
-      lds_v[buf][v_unit(row, 2 * c16)] = uint2{vst[p].x, vst[p].y};
-      lds_v[buf][v_unit(row, 2 * c16 + 1)] = uint2{vst[p].z, vst[p].w};
-    }
-  };
+    for (int ks = 0; ks < 4; ++ks) kofs[ks] = row * 128 + 16 * ((2 * ks + hl) ^ ((row >> 1) & 7));
+  }
+  // V^T (A operand of P V): channel row 32 dt + ln (dt adds 32 rows = 2 KB, same swizzle),
+  // keys 32 hl + 0..31 = logical chunks 2 hl, 2 hl + 1.
+  uint32_t vofs[2];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) vofs[c2] = ln * 64 + 16 * ((2 * hl + c2) ^ ((ln >> 2) & 3));
 
   const int n_kt = (S + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  const bool ragged = (S % BK) != 0;
 
-  for (int t = 0; t < n_kt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_kt) load_tile(t + 1);
+  // One key tile from LDS stage `stage` (a constant in the main loop, a runtime
+  // value for the last tile, which always goes through one code path so that
+  // nothing is merged between its last MFMA and the epilogue).
+  auto tile = [&](auto stage_v, auto tail_c, int t) {
+    constexpr bool tail = decltype(tail_c)::value;
+    const int stage = stage_v;
+    const DITATTN_LDS char* kb = (const DITATTN_LDS char*)(lds + stage * STAGE_BYTES);
+    const DITATTN_LDS char* vb = kb + KT_BYTES;
     const int j0 = t * BK;
 
     // ---- S^T = K Q^T (int32)
@@ -116,30 +150,31 @@ sage_attn_fwd_kernel(const int8_t* __restrict__ q_i8, const float* __restrict__ 
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       si[tt] = i32x16{};
-      const int row = 32 * tt + swap23(ln);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const i32x4 kf = __builtin_bit_cast(i32x4, lds_k[buf][k_chunk(row, 2 * ks + hl)]);
+        const i32x4 kf = *(const DITATTN_LDS i32x4*)(kb + kofs[ks] + tt * 16 * 128);
         si[tt] = mfma_i8_32x32x32(kf, qf[ks], si[tt]);
       }
     }
-    // accumulator register r of sub-tile tt holds key j0 + 32 tt + key_of(r)
-    //   key_of(r) = 8 hl + r (r < 8),  16 + 8 hl + (r - 8) (r >= 8)
-    float x[2][16];
-    float mx = -INFINITY;
+    // a lane's 32 keys (32 hl + 0..31) are exactly one 32-row K block
+    const float sc = sq * ksc[(j0 >> 5) + hl];
+    float x[32];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const float sc = sq * ksc[(j0 >> 5) + tt];
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[tt][r] = (float)si[tt][r] * sc;
-        const int j = j0 + 32 * tt + (r < 8 ? 8 * hl + r : 16 + 8 * hl + (r - 8));
-        if (j0 + BK > S && j >= S) x[tt][r] = -INFINITY;
-        mx = fmaxf(mx, x[tt][r]);
+      for (int r = 0; r < 16; ++r) x[16 * tt + r] = (float)si[tt][r] * sc;
+    if constexpr (tail) {
+      if (ragged) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          if (j0 + 32 * hl + e >= S) x[e] = -INFINITY;
       }
     }
+    float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+    for (int e = 2; e < 32; e += 2) mx = max3(mx, x[e], x[e + 1]);
     mx = half_pair_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazyThresh) != 0) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
@@ -148,43 +183,60 @@ sage_attn_fwd_kernel(const int8_t* __restrict__ q_i8, const float* __restrict__ 
       for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
     }
     const float mneg = kPScaleLog2 - m;
-    // P (B operand, 32 e4m3 bytes): element e -> sub-tile e / 16, register e % 16
+    // P (B operand, 32 e4m3 bytes): byte e = key 32 hl + e
     i32x8 pf;
-    float ps = 0.0f;
+    float p[32];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      float p4[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = 4 * w + u;
-        p4[u] = fast_exp2(x[e >> 4][e & 15] + mneg);
-        ps += p4[u];
-      }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], word, true);
+      for (int u = 0; u < 4; ++u) p[4 * w + u] = fast_exp2(x[4 * w + u] + mneg);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
       pf[w] = word;
     }
-    lsum += ps;
+    lsum += tree_sum<32>(p);
 
-    // ---- O^T += V^T P^T: A lane l = V^T[32 dt + ln][keys 8 hl + 16 q + 0..7, q = 0..3]
+    // ---- O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const int row = 32 * dt + ln;
-      i32x8 va;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const uint2 u = lds_v[buf][v_unit(row, hl + 2 * qq)];
-        va[2 * qq] = (int)u.x;
-        va[2 * qq + 1] = (int)u.y;
-      }
-      acc[dt] = mfma_fp8_32x32x64(va, pf, acc[dt]);
+      const i32x4 v0 = *(const DITATTN_LDS i32x4*)(vb + vofs[0] + dt * 32 * 64);
+      const i32x4 v1 = *(const DITATTN_LDS i32x4*)(vb + vofs[1] + dt * 32 * 64);
+      const i32x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[dt] = mfma_fp8_32x32x64(va, pf, acc[dt], unit_scale);
     }
+  };
 
-    if (t + 1 < n_kt) store_tile(buf ^ 1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using Full = std::integral_constant<bool, false>;
+  using Last = std::integral_constant<bool, true>;
+  const int n_main = n_kt - 1;  // tiles before the last one
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int t = 0;
+  for (; t + 1 < n_main; t += 2) {  // two tiles per trip: stage offsets are immediates
+    issue(t + 1, 1);
+    tile(I0{}, Full{}, t);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue(t + 2, 0);
+    tile(I1{}, Full{}, t + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  if (t < n_main) {  // one more tile before the last, in stage 0 (t is even)
+    issue(t + 1, 1);
+    tile(I0{}, Full{}, t);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    ++t;
+  }
+  tile(t & 1, Last{}, t);  // the last tile (masked when S is ragged)
 
   // ---- epilogue: O[i][d] = acc * v_scale[d] / l
+  mfma_drain(acc[0], acc[1], acc[2], acc[3]);
   const float inv = 1.0f / half_pair_sum(lsum);
   const int i = q0 + ln;
   if (i < S) {

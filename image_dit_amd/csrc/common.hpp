@@ -84,11 +84,29 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET) : "memory");
   return r;
 }
-// Wait for every outstanding LDS read and make the given registers depend on
-// the wait, so no consumer can be scheduled above it.
+// Wait until at most N LDS operations are outstanding and make the given
+// registers depend on the wait, so no consumer can be scheduled above it.
+template <int N>
 __device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d, u32x2& e,
                                          u32x2& f, u32x2& g, u32x2& h) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
+               : "i"(N));
+}
+
+// Pin a value at this point of the program: the empty volatile asm "changes"
+// it, so IR passes cannot sink the computation to a later use.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
+
+// Let the last MFMAs writing these accumulators retire before any VALU reads
+// them (64 wait states, the full latency of a 16-pass MFMA).  The padding this
+// compiler inserts after v_mfma_scale_f32_32x32x64_f8f6f4 is too short, and
+// the first epilogue reads then see stale registers.  The accumulators are
+// operands, so no read can be scheduled above the wait.
+__device__ __forceinline__ void mfma_drain(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
 // Round two fp32 values to BF16 (nearest even) and pack them, low half first.
@@ -103,9 +121,19 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 
 __device__ __forceinline__ i32x16 mfma_i8_32x32x32(i32x4 a, i32x4 b, i32x16 c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
-// FP8 (OCP e4m3) x FP8 -> FP32, 32x32x64; block scales fixed at 2^0.
-__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// E8M0 block scale 2^0 (= 127) held in a VGPR.  Produced by an opaque move so
+// the compiler keeps it as a live register operand: when the constant is
+// passed directly, this compiler has been seen to reuse the scale register for
+// other values in some code paths, which silently rescales rows of the result.
+__device__ __forceinline__ int unit_e8m0_scale() {
+  int s;
+  asm volatile("v_mov_b32 %0, 0x7f" : "=v"(s));
+  return s;
+}
+// FP8 (OCP e4m3) x FP8 -> FP32, 32x32x64, with the given E8M0 block scales
+// (pass unit_e8m0_scale() for no scaling).
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c, int scale) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale, 0, scale);
 }
 
 // Workgroup index remapped so that consecutive logical tiles land on the same
