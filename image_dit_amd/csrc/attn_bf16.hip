@@ -217,28 +217,43 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       lsum[g] += tree_sum<32>(p);
     }
 
-    // V^T fragments for one 16-key chunk: 4 channel tiles x 2 transposed reads
+    // V^T fragments, one 16-key chunk at a time (4 channel tiles x 2 transposed
+    // reads), double-buffered so the next chunk's reads overlap this chunk's MFMAs.
     const uint32_t vaddr = (uint32_t)(uintptr_t)(const DITATTN_LDS char*)vb;
-    auto pv_chunk = [&](auto cc_c) {
+    u32x2 fa[4][2], fb[4][2];
+    auto vread = [&](auto cc_c, u32x2 (&f)[4][2]) {
       constexpr int cc = decltype(cc_c)::value;
-      u32x2 r[4][2];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        r[dt][0] = ds_read_tr16_b64<(16 * cc) * 256>(vaddr + vofs[dt]);
-        r[dt][1] = ds_read_tr16_b64<(16 * cc + 8) * 256>(vaddr + vofs[dt]);
+        f[dt][0] = ds_read_tr16_b64<(16 * cc) * 256>(vaddr + vofs[dt]);
+        f[dt][1] = ds_read_tr16_b64<(16 * cc + 8) * 256>(vaddr + vofs[dt]);
       }
-      lds_wait<0>(r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]);
+    };
+    auto pv_chunk = [&](auto cc_c, u32x2 (&f)[4][2]) {
+      constexpr int cc = decltype(cc_c)::value;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{r[dt][0][0], r[dt][0][1], r[dt][1][0], r[dt][1][1]});
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{f[dt][0][0], f[dt][0][1], f[dt][1][0], f[dt][1][1]});
 #pragma unroll
         for (int g = 0; g < QG; ++g) acc[g][dt] = mfma_bf16_32x32x16(va, pf[g][cc], acc[g][dt]);
       }
     };
-    pv_chunk(std::integral_constant<int, 0>{});
-    pv_chunk(std::integral_constant<int, 1>{});
-    pv_chunk(std::integral_constant<int, 2>{});
-    pv_chunk(std::integral_constant<int, 3>{});
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    vread(C0{}, fa);
+    vread(C1{}, fb);
+    lds_wait<8>(fa[0][0], fa[0][1], fa[1][0], fa[1][1], fa[2][0], fa[2][1], fa[3][0], fa[3][1]);
+    pv_chunk(C0{}, fa);
+    vread(C2{}, fa);
+    lds_wait<8>(fb[0][0], fb[0][1], fb[1][0], fb[1][1], fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
+    pv_chunk(C1{}, fb);
+    vread(C3{}, fb);
+    lds_wait<8>(fa[0][0], fa[0][1], fa[1][0], fa[1][1], fa[2][0], fa[2][1], fa[3][0], fa[3][1]);
+    pv_chunk(C2{}, fa);
+    lds_wait<0>(fb[0][0], fb[0][1], fb[1][0], fb[1][1], fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
+    pv_chunk(C3{}, fb);
   };
 
   using I0 = std::integral_constant<int, 0>;

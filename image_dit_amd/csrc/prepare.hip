@@ -12,10 +12,11 @@
 // All of it is HBM-bound, so the kernels are shaped for coalescing:
 //   quant_qk   one wave per (b, h, 32-row block) of Q or K: 32 rows x 256 B in,
 //              4 KB of codes out (contiguous), one scale.
-//   v_absmax   per (b, 256-token chunk): every thread keeps the running |v| max
-//              of 8 channels over the chunk (rows are H x 256 B contiguous),
-//              then one atomicMax per channel on the fp32 bit pattern (order
-//              free: max of non-negative floats = max of their bit patterns).
+//   v_absmax   per (b, token range, 512 channels): running |v| maxima in
+//              registers, combined across the 4 waves in LDS, then one
+//              atomicMax per channel on the fp32 bit pattern (order free: max
+//              of non-negative floats = max of their bit patterns).  The
+//              accumulator is cleared by quant_qk, which runs first.
 //   v_quant    per (b, h, 128-token chunk): quantize, transpose through LDS,
 //              write 128 channel rows of 128 B.
 //   v_finalize v_scale = absmax / 448 in place.
@@ -40,7 +41,12 @@ __device__ __forceinline__ float wave_max(float x) {
 __global__ void __launch_bounds__(256)
 quant_qk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 int8_t* __restrict__ q_i8, float* __restrict__ q_scale, int8_t* __restrict__ k_i8,
-                float* __restrict__ k_scale, int S, int H, int nblk, int units, float c) {
+                float* __restrict__ k_scale, int S, int H, int nblk, int units, float c,
+                uint32_t* __restrict__ amax_bits, int n_amax) {
+  // clear the V absmax accumulator for v_absmax_kernel, which runs next on the stream
+  for (int i = (blockIdx.y * gridDim.x + blockIdx.x) * 256 + threadIdx.x; i < n_amax; i += gridDim.x * gridDim.y * 256)
+    amax_bits[i] = 0u;
+
   const bool is_q = blockIdx.y == 0;
   const uint16_t* x = is_q ? q : k;
   int8_t* codes = is_q ? q_i8 : k_i8;
@@ -95,47 +101,53 @@ quant_qk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 // ---------------------------------------------------------------- V absmax
-constexpr int kAbsTok = 256;  // tokens per v_absmax workgroup
-
+// grid (ceil(S / tok_per_wg), ceil(H * 16 / 64), B), 256 threads.  Thread t owns
+// chunk column blockIdx.y * 64 + (t & 63) (8 channels) and tokens
+// j0 + (t >> 6) + 4 k: a wave reads 1 KB of one token row.  The 4 waves combine
+// their maxima in LDS, then one atomicMax per channel on the fp32 bit pattern
+// of |v|.  amax_bits: [B, H, 128], cleared by quant_qk_kernel, which runs first.
 __global__ void __launch_bounds__(256)
-fill_zero_kernel(uint32_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
-// grid (ceil(S / kAbsTok), ceil(H * 16 / 256), B); amax_bits: [B, H, 128] fp32
-// bit patterns, zeroed.  Thread -> one 16-byte chunk column (8 channels of one
-// head) over kAbsTok tokens, 8 loads in flight.
-__global__ void __launch_bounds__(256)
-v_absmax_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits, int S, int H) {
+v_absmax_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits, int S, int H,
+                int tok_per_wg) {
+  __shared__ uint32_t red[4][64][8];
   const int b = blockIdx.z;
-  const int col = blockIdx.y * 256 + threadIdx.x;
   const int ncol = H * 16;  // 16-byte chunks per token row (all heads)
-  if (col >= ncol) return;
-  const int j0 = blockIdx.x * kAbsTok;
-  const int j1 = min(j0 + kAbsTok, S);
+  const int col = blockIdx.y * 64 + (threadIdx.x & 63);
+  const int wv = threadIdx.x >> 6;
+  const int j0 = blockIdx.x * tok_per_wg;
+  const int j1 = min(j0 + tok_per_wg, S);
   const int64_t tok = (int64_t)H * kHeadDim;
-  const uint16_t* src = v + (int64_t)b * S * tok + 8 * col;
   uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // |v| as bf16 magnitude bits
-  for (int j = j0; j < j1; j += 8) {
-    uint4 raw[8];
+  if (col < ncol) {
+    const uint16_t* src = v + (int64_t)b * S * tok + 8 * col;
+    for (int j = j0 + wv; j < j1; j += 16) {
+      uint4 raw[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) raw[u] = (j + u < j1) ? *(const uint4*)(src + (j + u) * tok) : uint4{0, 0, 0, 0};
+      for (int u = 0; u < 4; ++u) raw[u] = (j + 4 * u < j1) ? *(const uint4*)(src + (j + 4 * u) * tok) : uint4{0, 0, 0, 0};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        mx[2 * e] = max(mx[2 * e], w[e] & 0x7FFFu);
-        mx[2 * e + 1] = max(mx[2 * e + 1], (w[e] >> 16) & 0x7FFFu);
+        for (int e = 0; e < 4; ++e) {
+          mx[2 * e] = max(mx[2 * e], w[e] & 0x7FFFu);
+          mx[2 * e + 1] = max(mx[2 * e + 1], (w[e] >> 16) & 0x7FFFu);
+        }
       }
     }
   }
-  // bf16 magnitude bits << 16 = fp32 bits of |v|; finite magnitudes order like integers
-  uint32_t* dst = amax_bits + (int64_t)b * H * kHeadDim + 8 * col;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (mx[e] != 0u) atomicMax(dst + e, mx[e] << 16);
+  for (int e = 0; e < 8; ++e) red[wv][threadIdx.x & 63][e] = mx[e];
+  __syncthreads();
+  // 64 columns x 8 channels = 512 maxima, two per thread
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int c = idx >> 3, e = idx & 7;
+    const uint32_t m4 = max(max(red[0][c][e], red[1][c][e]), max(red[2][c][e], red[3][c][e]));
+    const int gcol = blockIdx.y * 64 + c;
+    // bf16 magnitude bits << 16 = fp32 bits of |v|; finite magnitudes order like integers
+    if (gcol < ncol && m4 != 0u) atomicMax(amax_bits + (int64_t)b * H * kHeadDim + 8 * gcol + e, m4 << 16);
+  }
 }
 
 // ---------------------------------------------------------------- V quantize + transpose
@@ -215,12 +227,16 @@ hipError_t launch_sage_prepare(const void* q, const void* k, const void* v, int8
   const int units = B * H * nblk;
   const int nscale = B * H * kHeadDim;
   uint32_t* amax_bits = reinterpret_cast<uint32_t*>(v_scale);
-  hipLaunchKernelGGL(prep::fill_zero_kernel, dim3((nscale + 255) / 256), dim3(256), 0, stream, amax_bits, nscale);
   hipLaunchKernelGGL(prep::quant_qk_kernel, dim3((units + 3) / 4, 2), dim3(256), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, q_i8, q_scale, k_i8, k_scale, S, H, nblk,
-                     units, c);
-  hipLaunchKernelGGL(prep::v_absmax_kernel, dim3((S + prep::kAbsTok - 1) / prep::kAbsTok, (H * 16 + 255) / 256, B),
-                     dim3(256), 0, stream, (const uint16_t*)v, amax_bits, S, H);
+                     units, c, amax_bits, nscale);
+  // V absmax: about 1000 workgroups whatever the shape, token ranges a multiple of 16
+  const int colblk = (H * 16 + 63) / 64;
+  int tok_per_wg = (int)(((int64_t)S * colblk * B + 1023) / 1024);
+  tok_per_wg = (tok_per_wg + 15) / 16 * 16;
+  if (tok_per_wg < 16) tok_per_wg = 16;
+  hipLaunchKernelGGL(prep::v_absmax_kernel, dim3((S + tok_per_wg - 1) / tok_per_wg, colblk, B), dim3(256), 0,
+                     stream, (const uint16_t*)v, amax_bits, S, H, tok_per_wg);
   hipLaunchKernelGGL(prep::v_quant_kernel, dim3(S_pad / prep::kVTok, B * H), dim3(256), 0, stream,
                      (const uint16_t*)v, (const uint32_t*)amax_bits, v_fp8, S, H, S_pad);
   hipLaunchKernelGGL(prep::v_finalize_kernel, dim3((nscale + 255) / 256), dim3(256), 0, stream, v_scale, nscale);
