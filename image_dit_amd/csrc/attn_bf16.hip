@@ -43,14 +43,25 @@ namespace bf16attn {
 
 // Tuning knobs (compile-time; defaults are the measured choice).
 #ifndef DITATTN_BF16_OCC
-#define DITATTN_BF16_OCC 2  // workgroups per CU the register budget is sized for
+#define DITATTN_BF16_OCC 1  // workgroups per CU the register budget is sized for
 #endif
 #ifndef DITATTN_BF16_QG
 #define DITATTN_BF16_QG 1   // 32-row query groups per wave
 #endif
 
+#ifndef DITATTN_BF16_NW
+#define DITATTN_BF16_NW 8   // waves per workgroup (all share one K/V tile); 2 per SIMD
+#endif
+#ifndef DITATTN_BF16_NSTAGE
+#define DITATTN_BF16_NSTAGE 2  // K/V tiles resident in LDS (copies run NSTAGE - 1 tiles ahead)
+#endif
+
 constexpr int BK = 64;      // keys per K/V tile
-constexpr int NW = 4;       // waves per workgroup
+constexpr int NW = DITATTN_BF16_NW;
+constexpr int RPW = BK / NW;   // tile rows each wave copies
+constexpr int NCP = RPW / 4;   // 1 KB copy instructions per wave per tile (K or V)
+constexpr int NSTAGE = DITATTN_BF16_NSTAGE;
+static_assert(NSTAGE >= 2 && NSTAGE <= 4, "LDS holds at most 4 stages of 32 KB");
 constexpr int ROW_CHUNKS = 16;  // 16-byte chunks per 128-channel BF16 row
 constexpr float kLazyThresh = 8.0f;
 
@@ -65,14 +76,15 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o, int S, int H, float c,
                      int num_qt, int n_tiles) {
   constexpr int BQ = NW * QG * 32;
-  __shared__ __attribute__((aligned(16))) char lds[2 * BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * BUF_BYTES];
 
   const int L = xcd_remap(blockIdx.x, n_tiles);
   const int bh = L / num_qt;
   const int qt = L - bh * num_qt;
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, l = tid & 63, hl = l >> 5, ln = l & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, hl = l >> 5, ln = l & 31;
   const int64_t tok = (int64_t)H * kHeadDim;  // elements between consecutive tokens
   const uint32_t tok_bytes = (uint32_t)(tok * 2);
   const int64_t base = ((int64_t)b * S * H + h) * kHeadDim;
@@ -104,24 +116,33 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int dt = 0; dt < 4; ++dt) acc[g][dt] = f32x16{};
   }
 
-  // ---- global -> LDS (direct).  Wave w, instruction n writes LDS rows 16 w + 4 n + l / 16,
+  // ---- global -> LDS (direct).  Wave w, instruction n writes LDS rows RPW w + 4 n + l / 16,
   // physical chunk l % 16; the lane fetches the logical chunk that lands there.
   const int p_chunk = l & 15;
+  uint32_t koff[NCP], voff[NCP];  // this lane's source offsets in a full tile
+#pragma unroll
+  for (int n = 0; n < NCP; ++n) {
+    const int r = RPW * wave + 4 * n + (l >> 4);
+    koff[n] = r * tok_bytes + 16u * (uint32_t)(p_chunk ^ (r & 15));
+    voff[n] = r * tok_bytes + 16u * (uint32_t)(p_chunk ^ ((r & 3) << 2));
+  }
   auto issue_tile = [&](int t, int buf, bool clamp) {
     const int j0 = t * BK;
     const char* kt = kbh + (int64_t)j0 * tok * 2;
     const char* vt = vbh + (int64_t)j0 * tok * 2;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int r = 16 * wave + 4 * n + (l >> 4);
-      int rr = r;
-      if (clamp && j0 + r >= S) rr = S - 1 - j0;  // rows past the end repeat the last real key
-      const uint32_t koff = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ (r & 15));
-      const uint32_t voff = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ ((r & 3) << 2));
-      char* kdst = lds + buf * BUF_BYTES + (16 * wave + 4 * n) * 256;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + koff),
+    for (int n = 0; n < NCP; ++n) {
+      uint32_t ko = koff[n], vo = voff[n];
+      if (clamp) {  // rows past the end repeat the last real key
+        const int r = RPW * wave + 4 * n + (l >> 4);
+        const int rr = (j0 + r >= S) ? S - 1 - j0 : r;
+        ko = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ (r & 15));
+        vo = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ ((r & 3) << 2));
+      }
+      char* kdst = lds + buf * BUF_BYTES + (RPW * wave + 4 * n) * 256;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + ko),
                                        (DITATTN_LDS void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + voff),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + vo),
                                        (DITATTN_LDS void*)(kdst + TILE_BYTES), 16, 0, 0);
     }
   };
@@ -256,35 +277,51 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     pv_chunk(C3{}, fb);
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
   using Full = std::integral_constant<bool, false>;
   using Last = std::integral_constant<bool, true>;
   const int n_main = n_kt - 1;  // tiles before the last one
+  constexpr int kCopies = 2 * NCP;  // copy instructions per wave per tile
 
-  issue_tile(0, 0, n_kt == 1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile loads have landed in LDS
+  // Prologue: tiles 0 .. NSTAGE-2 in flight, wait for all of them once.
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p)
+    if (p < n_kt) issue_tile(p, p, p == n_kt - 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+
+  // Iteration t: refill the stage freed by tile t-1 with tile t+NSTAGE-1, compute
+  // tile t, then wait until this wave's copies of tile t+1 have landed.
+  auto step = [&](auto buf_c, int t) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int nxt = t + NSTAGE - 1;
+    const bool refill = nxt < n_kt;
+    if (refill) issue_tile(nxt, (buf + NSTAGE - 1) % NSTAGE, nxt == n_kt - 1);
+    tile(buf_c, Full{}, t);
+    if (refill) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"i"((NSTAGE - 2) * kCopies) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+  };
+  // NSTAGE tiles per trip so the stage offsets are immediates; the trip is
+  // left as soon as only the last tile remains.
   int t = 0;
-  // two tiles per trip so the buffer offsets are immediates
-  for (; t + 1 < n_main; t += 2) {
-    issue_tile(t + 1, 1, false);
-    tile(I0{}, Full{}, t);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue_tile(t + 2, 0, t + 2 == n_kt - 1);
-    tile(I1{}, Full{}, t + 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  while (true) {
+    if (t >= n_main) break;
+    step(std::integral_constant<int, 0>{}, t++);
+    if (t >= n_main) break;
+    step(std::integral_constant<int, 1>{}, t++);
+    if constexpr (NSTAGE > 2) {
+      if (t >= n_main) break;
+      step(std::integral_constant<int, 2 % NSTAGE>{}, t++);
+    }
+    if constexpr (NSTAGE > 3) {
+      if (t >= n_main) break;
+      step(std::integral_constant<int, 3 % NSTAGE>{}, t++);
+    }
   }
-  if (t < n_main) {  // one more tile before the last, in buffer 0 (t is even)
-    issue_tile(t + 1, 1, true);
-    tile(I0{}, Full{}, t);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    ++t;
-  }
-  tile(t & 1, Last{}, t);  // the last tile (masked when S is ragged)
+  tile(t % NSTAGE, Last{}, t);  // the last tile (masked when S is ragged)
 
   // ---- epilogue: O = acc / l, BF16, rows < S
 #pragma unroll
