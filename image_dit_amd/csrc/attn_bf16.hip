@@ -45,38 +45,30 @@ namespace bf16attn {
 #ifndef DITATTN_BF16_OCC
 #define DITATTN_BF16_OCC 1  // workgroups per CU the register budget is sized for
 #endif
-#ifndef DITATTN_BF16_QG
-#define DITATTN_BF16_QG 1   // 32-row query groups per wave
-#endif
 
 #ifndef DITATTN_BF16_NW
 #define DITATTN_BF16_NW 8   // waves per workgroup (all share one K/V tile); 2 per SIMD
-#endif
-#ifndef DITATTN_BF16_NSTAGE
-#define DITATTN_BF16_NSTAGE 2  // K/V tiles resident in LDS (copies run NSTAGE - 1 tiles ahead)
 #endif
 
 constexpr int BK = 64;      // keys per K/V tile
 constexpr int NW = DITATTN_BF16_NW;
 constexpr int RPW = BK / NW;   // tile rows each wave copies
 constexpr int NCP = RPW / 4;   // 1 KB copy instructions per wave per tile (K or V)
-constexpr int NSTAGE = DITATTN_BF16_NSTAGE;
-static_assert(NSTAGE >= 2 && NSTAGE <= 4, "LDS holds at most 4 stages of 32 KB");
-constexpr int ROW_CHUNKS = 16;  // 16-byte chunks per 128-channel BF16 row
+static_assert(NW == 8, "the ping-pong pairs waves w and w + 4 on one SIMD");
 constexpr float kLazyThresh = 8.0f;
 
 
-// Byte layout of the LDS ring: [buf][K | V][64 rows x 256 B].
+// LDS: two K stages then two V stages, each 64 rows x 256 B.
 constexpr int TILE_BYTES = BK * 256;
-constexpr int BUF_BYTES = 2 * TILE_BYTES;
+constexpr int K_STAGE0 = 0;
+constexpr int V_STAGE0 = 2 * TILE_BYTES;
 
-template <int QG>
 __global__ void __launch_bounds__(NW * 64, DITATTN_BF16_OCC)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o, int S, int H, float c,
                      int num_qt, int n_tiles) {
-  constexpr int BQ = NW * QG * 32;
-  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * BUF_BYTES];
+  constexpr int BQ = NW * 32;
+  __shared__ __attribute__((aligned(16))) char lds[4 * TILE_BYTES];  // K stage 0, 1, V stage 0, 1
 
   const int L = xcd_remap(blockIdx.x, n_tiles);
   const int bh = L / num_qt;
@@ -93,28 +85,20 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const char* vbh = (const char*)(v + base);
   __bf16* obh = o + base;
 
-  // Q^T operand, resident for the whole key loop: Q[q0 + 32 g + ln][16 ks + 8 hl + 0..7].
-  const int q0 = qt * BQ + wave * QG * 32;
-  bf16x8 qf[QG][8];
+  // Q^T operand, resident for the whole key loop: Q[q0 + ln][16 ks + 8 hl + 0..7].
+  const int q0 = qt * BQ + wave * 32;
+  const int qi = q0 + ln;  // this lane's query row
+  bf16x8 qf[8];
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const int i = q0 + 32 * g + ln;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (i < S) qf[g][ks] = *(const bf16x8*)(qbh + i * tok + 16 * ks + 8 * hl);
-      else qf[g][ks] = bf16x8{};
-    }
+  for (int ks = 0; ks < 8; ++ks) {
+    if (qi < S) qf[ks] = *(const bf16x8*)(qbh + qi * tok + 16 * ks + 8 * hl);
+    else qf[ks] = bf16x8{};
   }
 
-  f32x16 acc[QG][4];
-  float m[QG], lsum[QG];
+  f32x16 acc[4];  // O^T: channels 32 dt + (accumulator row), this lane's query
+  float m = -INFINITY, lsum = 0.0f;
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    m[g] = -INFINITY;
-    lsum[g] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[g][dt] = f32x16{};
-  }
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
   // ---- global -> LDS (direct).  Wave w, instruction n writes LDS rows RPW w + 4 n + l / 16,
   // physical chunk l % 16; the lane fetches the logical chunk that lands there.
@@ -126,24 +110,25 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     koff[n] = r * tok_bytes + 16u * (uint32_t)(p_chunk ^ (r & 15));
     voff[n] = r * tok_bytes + 16u * (uint32_t)(p_chunk ^ ((r & 3) << 2));
   }
-  auto issue_tile = [&](int t, int buf, bool clamp) {
+  // Copy key tile t of K (is_v false) or V (is_v true) into the LDS stage at byte
+  // offset dst.  In the ragged last tile, rows past the end repeat the last real
+  // key: finite data whose scores are masked to -inf (so P = 0 against it).
+  const int n_kt = (S + BK - 1) / BK;
+  const bool ragged = (S % BK) != 0;
+  auto issue = [&](const char* src, int t, int dst, bool is_v) {
     const int j0 = t * BK;
-    const char* kt = kbh + (int64_t)j0 * tok * 2;
-    const char* vt = vbh + (int64_t)j0 * tok * 2;
+    const char* st = src + (int64_t)j0 * tok * 2;
+    const bool clamp = ragged && t == n_kt - 1;
 #pragma unroll
     for (int n = 0; n < NCP; ++n) {
-      uint32_t ko = koff[n], vo = voff[n];
-      if (clamp) {  // rows past the end repeat the last real key
+      uint32_t off = is_v ? voff[n] : koff[n];
+      if (clamp) {
         const int r = RPW * wave + 4 * n + (l >> 4);
         const int rr = (j0 + r >= S) ? S - 1 - j0 : r;
-        ko = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ (r & 15));
-        vo = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ ((r & 3) << 2));
+        off = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ (is_v ? (r & 3) << 2 : r & 15));
       }
-      char* kdst = lds + buf * BUF_BYTES + (RPW * wave + 4 * n) * 256;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + ko),
-                                       (DITATTN_LDS void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + vo),
-                                       (DITATTN_LDS void*)(kdst + TILE_BYTES), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(st + off),
+                                       (DITATTN_LDS void*)(lds + dst + (RPW * wave + 4 * n) * 256), 16, 0, 0);
     }
   };
 
@@ -164,192 +149,235 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   }
 
-  const int n_kt = (S + BK - 1) / BK;
-  const bool ragged = (S % BK) != 0;
-
-  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  // One key tile from LDS buffer `buf` (a constant in the main loop, a runtime
-  // value for the last tile, which always goes through one code path so that
-  // nothing is merged between its last MFMA and the epilogue).
-  auto tile = [&](auto buf_v, auto tail_c, int t) {
-    constexpr bool tail = decltype(tail_c)::value;
-    const int buf = buf_v;
-    const char* kb = lds + buf * BUF_BYTES;
-    const char* vb = kb + TILE_BYTES;
-
-    f32x16 s[2][QG];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int g = 0; g < QG; ++g) s[tt][g] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 kf = *(const DITATTN_LDS bf16x8*)((const DITATTN_LDS char*)kb + kofs[ks] + tt * 32 * 256);
-#pragma unroll
-        for (int g = 0; g < QG; ++g) s[tt][g] = mfma_bf16_32x32x16(kf, qf[g][ks], s[tt][g]);
-      }
-    }
-    if constexpr (tail) {
-      if (ragged) {
-        const int j0 = t * BK;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 32 * tt + 8 * (r >> 2) + 4 * hl + (r & 3);
-#pragma unroll
-            for (int g = 0; g < QG; ++g)
-              if (j >= S) s[tt][g][r] = -INFINITY;
-          }
-      }
-    }
-
-    bf16x8 pf[QG][4];
-#pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      float mx = fmaxf(s[0][g][0], s[1][g][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = max3(mx, s[0][g][r], s[1][g][r]);
-      mx = half_pair_max(mx) * c;
-      // raise the running max only when it grew by more than the threshold
-      if (__builtin_amdgcn_ballot_w64(mx > m[g] + kLazyThresh) != 0) {
-        const float m_new = fmaxf(m[g], mx);
-        const float alpha = fast_exp2(m[g] - m_new);
-        m[g] = m_new;
-        lsum[g] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[g][dt] *= alpha;
-      }
-      const float mneg = -m[g];
-      float p[32];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[16 * tt + r] = fast_exp2(fmaf(s[tt][g][r], c, mneg));
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        bf16x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = (__bf16)p[8 * cc + e];
-        pf[g][cc] = pv;
-      }
-      lsum[g] += tree_sum<32>(p);
-    }
-
-    // V^T fragments, one 16-key chunk at a time (4 channel tiles x 2 transposed
-    // reads), double-buffered so the next chunk's reads overlap this chunk's MFMAs.
-    const uint32_t vaddr = (uint32_t)(uintptr_t)(const DITATTN_LDS char*)vb;
-    u32x2 fa[4][2], fb[4][2];
-    auto vread = [&](auto cc_c, u32x2 (&f)[4][2]) {
-      constexpr int cc = decltype(cc_c)::value;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        f[dt][0] = ds_read_tr16_b64<(16 * cc) * 256>(vaddr + vofs[dt]);
-        f[dt][1] = ds_read_tr16_b64<(16 * cc + 8) * 256>(vaddr + vofs[dt]);
-      }
-    };
-    auto pv_chunk = [&](auto cc_c, u32x2 (&f)[4][2]) {
-      constexpr int cc = decltype(cc_c)::value;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{f[dt][0][0], f[dt][0][1], f[dt][1][0], f[dt][1][1]});
-#pragma unroll
-        for (int g = 0; g < QG; ++g) acc[g][dt] = mfma_bf16_32x32x16(va, pf[g][cc], acc[g][dt]);
+  // ---- matrix phase: O^T += V^T P^T for the keys of V stage VS (16 MFMA, 32
+  // transposed reads) and/or S^T = K Q^T for the keys of K stage KS (16 MFMA, 16
+  // reads), as one explicitly pipelined stream: V fragments one 16-key chunk
+  // ahead, K fragments three channel steps ahead, and the first K reads issued
+  // under the last P V chunks.  Waits count outstanding LDS reads (returned in order).
+  f32x16 sc[2];  // scores of the latest tile, one 32-key sub-tile each
+  bf16x8 pf[4];  // P of the latest softmax, one 16-key chunk each
+  auto mphase = [&](auto vs_c, auto ks_c, auto pv_c, auto qk_c) {
+    constexpr int VS = decltype(vs_c)::value, KS = decltype(ks_c)::value;
+    constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
+    constexpr int VB = V_STAGE0 + VS * TILE_BYTES, KB = K_STAGE0 + KS * TILE_BYTES;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const DITATTN_LDS char*)lds;
+    u32x4 kf[8][2];
+    auto kread = [&](auto s_c) {
+      constexpr int st = decltype(s_c)::value;
+      if constexpr (st < 8) {
+        kf[st][0] = ds_read_b128<KB>(lds0 + kofs[st]);
+        kf[st][1] = ds_read_b128<KB + 32 * 256>(lds0 + kofs[st]);
       }
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
     using C3 = std::integral_constant<int, 3>;
-    vread(C0{}, fa);
-    vread(C1{}, fb);
-    lds_wait<8>(fa[0][0], fa[0][1], fa[1][0], fa[1][1], fa[2][0], fa[2][1], fa[3][0], fa[3][1]);
-    pv_chunk(C0{}, fa);
-    vread(C2{}, fa);
-    lds_wait<8>(fb[0][0], fb[0][1], fb[1][0], fb[1][1], fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
-    pv_chunk(C1{}, fb);
-    vread(C3{}, fb);
-    lds_wait<8>(fa[0][0], fa[0][1], fa[1][0], fa[1][1], fa[2][0], fa[2][1], fa[3][0], fa[3][1]);
-    pv_chunk(C2{}, fa);
-    lds_wait<0>(fb[0][0], fb[0][1], fb[1][0], fb[1][1], fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
-    pv_chunk(C3{}, fb);
-  };
-
-  using Full = std::integral_constant<bool, false>;
-  using Last = std::integral_constant<bool, true>;
-  const int n_main = n_kt - 1;  // tiles before the last one
-  constexpr int kCopies = 2 * NCP;  // copy instructions per wave per tile
-
-  // Prologue: tiles 0 .. NSTAGE-2 in flight, wait for all of them once.
+    if constexpr (PV) {
+      u32x2 fa[4][2], fb[4][2];
+      auto vread = [&](auto cc_c, u32x2 (&f)[4][2]) {
+        constexpr int cc = decltype(cc_c)::value;
 #pragma unroll
-  for (int p = 0; p < NSTAGE - 1; ++p)
-    if (p < n_kt) issue_tile(p, p, p == n_kt - 1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  // Iteration t: refill the stage freed by tile t-1 with tile t+NSTAGE-1, compute
-  // tile t, then wait until this wave's copies of tile t+1 have landed.
-  auto step = [&](auto buf_c, int t) {
-    constexpr int buf = decltype(buf_c)::value;
-    const int nxt = t + NSTAGE - 1;
-    const bool refill = nxt < n_kt;
-    if (refill) issue_tile(nxt, (buf + NSTAGE - 1) % NSTAGE, nxt == n_kt - 1);
-    tile(buf_c, Full{}, t);
-    if (refill) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"i"((NSTAGE - 2) * kCopies) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int dt = 0; dt < 4; ++dt) {
+          f[dt][0] = ds_read_tr16_b64<VB + (16 * cc) * 256>(lds0 + vofs[dt]);
+          f[dt][1] = ds_read_tr16_b64<VB + (16 * cc + 8) * 256>(lds0 + vofs[dt]);
+        }
+      };
+      auto chunk = [&](auto cc_c, u32x2 (&f)[4][2]) {
+        constexpr int cc = decltype(cc_c)::value;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{f[dt][0][0], f[dt][0][1], f[dt][1][0], f[dt][1][1]});
+          acc[dt] = mfma_bf16_32x32x16(va, pf[cc], acc[dt]);
+        }
+      };
+      vread(C0{}, fa);
+      vread(C1{}, fb);
+      lds_wait<8>(fa[0][0], fa[0][1], fa[1][0], fa[1][1], fa[2][0], fa[2][1], fa[3][0], fa[3][1]);
+      chunk(C0{}, fa);
+      vread(C2{}, fa);
+      lds_wait<8>(fb[0][0], fb[0][1], fb[1][0], fb[1][1], fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
+      chunk(C1{}, fb);
+      vread(C3{}, fb);
+      lds_wait<8>(fa[0][0], fa[0][1], fa[1][0], fa[1][1], fa[2][0], fa[2][1], fa[3][0], fa[3][1]);
+      chunk(C2{}, fa);
+      if constexpr (QK) {
+        kread(C0{});
+        kread(C1{});
+        kread(C2{});
+        lds_wait<6>(fb[0][0], fb[0][1], fb[1][0], fb[1][1], fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
+      } else {
+        lds_wait<0>(fb[0][0], fb[0][1], fb[1][0], fb[1][1], fb[2][0], fb[2][1], fb[3][0], fb[3][1]);
+      }
+      chunk(C3{}, fb);
+    } else if constexpr (QK) {
+      kread(C0{});
+      kread(C1{});
+      kread(C2{});
     }
-    __syncthreads();
+    if constexpr (QK) {
+      sc[0] = f32x16{};
+      sc[1] = f32x16{};
+      auto step = [&](auto s_c) {
+        constexpr int st = decltype(s_c)::value;
+        constexpr int later = 2 * ((st + 2 < 7 ? st + 2 : 7) - st);  // reads issued after step st's
+        lds_wait<later>(kf[st][0], kf[st][1]);
+        sc[0] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, kf[st][0]), qf[st], sc[0]);
+        sc[1] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, kf[st][1]), qf[st], sc[1]);
+        kread(std::integral_constant<int, st + 3>{});
+      };
+      step(C0{});
+      step(C1{});
+      step(C2{});
+      step(C3{});
+      step(std::integral_constant<int, 4>{});
+      step(std::integral_constant<int, 5>{});
+      step(std::integral_constant<int, 6>{});
+      step(std::integral_constant<int, 7>{});
+      pin(sc[0]);
+      pin(sc[1]);
+    }
+    if constexpr (PV) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) pin(acc[dt]);
+    }
   };
-  // NSTAGE tiles per trip so the stage offsets are immediates; the trip is
-  // left as soon as only the last tile remains.
-  int t = 0;
-  while (true) {
-    if (t >= n_main) break;
-    step(std::integral_constant<int, 0>{}, t++);
-    if (t >= n_main) break;
-    step(std::integral_constant<int, 1>{}, t++);
-    if constexpr (NSTAGE > 2) {
-      if (t >= n_main) break;
-      step(std::integral_constant<int, 2 % NSTAGE>{}, t++);
+  // softmax of the scores of tile q (in sc): mask the ragged end, raise the running
+  // max lazily (rescaling acc and l, whose last update is complete), P -> BF16.
+  auto softmax = [&](int q) {
+    if (ragged && q == n_kt - 1) {
+      // keys 32 tt + 8 (r / 4) + 4 hl + r % 4 of the tile are real below lim + 4 hl; the
+      // opaque move keeps the 32 compares here instead of hoisted out of the key loop
+      int lim = S - q * BK - 4 * hl;
+      asm volatile("" : "+v"(lim));
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * tt + 8 * (r >> 2) + (r & 3) >= lim) sc[tt][r] = -INFINITY;
     }
-    if constexpr (NSTAGE > 3) {
-      if (t >= n_main) break;
-      step(std::integral_constant<int, 3 % NSTAGE>{}, t++);
+    float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = max3(mx, sc[0][r], sc[1][r]);
+    mx = half_pair_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazyThresh) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
     }
+    const float mneg = -m;
+    float p[32];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[16 * tt + r] = fast_exp2(fmaf(sc[tt][r], c, mneg));
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      bf16x8 v8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v8[e] = (__bf16)p[8 * cc + e];
+      pf[cc] = v8;
+    }
+    lsum += tree_sum<32>(p);
+    // keep the softmax in its phase: without the pins the compiler sinks the
+    // exponentials past the barrier, next to the P V products that consume them
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) pin(pf[cc]);
+    pin(lsum);
+  };
+
+  // ---- ping-pong over key tiles.  Waves w and w + 4 share a SIMD.  Every wave runs
+  // the same sequence  M(0) | V(0) | M(1) | V(1) | ... | M(n)  with a barrier after
+  // each phase, where M(p) = [P V of tile p-1, K Q^T of tile p] (32 MFMA) and
+  // V(p) = softmax of tile p (VALU).  Group B (waves 4-7) starts one barrier late,
+  // so on each SIMD one wave's matrix phase overlaps the other's softmax.
+  // Barrier k: group A has finished phase k-1 of its sequence, group B phase k-2.
+  // K(q+1) and V(q) are copied in the window between barriers 2q and 2q+2 (issued
+  // at its start, awaited at its end): the stages they overwrite (K(q-1), V(q-2))
+  // were last read in M(q-1), which both groups finished by barrier 2q, and their
+  // first readers (M(q+1) of group A) start at barrier 2q+2.
+  const bool grp_a = wave < NW / 2;
+  auto copy = [&](int q) {  // K(q+1) and V(q), where they exist
+    if (q + 1 < n_kt) issue(kbh, q + 1, K_STAGE0 + ((q + 1) & 1) * TILE_BYTES, false);
+    if (q < n_kt) issue(vbh, q, V_STAGE0 + (q & 1) * TILE_BYTES, true);
+  };
+  auto copies_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // s_barrier without the release fence of __syncthreads(), which would also wait
+  // for the copies in flight; LDS reads before it have all been consumed.
+  auto barrier = [&]() { asm volatile("s_barrier" ::: "memory"); };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  // one period p (1 <= p <= n_kt - 1) with compile-time K stage par = p & 1
+  auto period = [&](auto par_c, int p) {
+    constexpr int par = decltype(par_c)::value;
+    using KS = std::integral_constant<int, par>;
+    using VS = std::integral_constant<int, par ^ 1>;
+    if (grp_a) copy(p);  // window 2p .. 2p+2
+    mphase(VS{}, KS{}, T{}, T{});
+    if (!grp_a) copies_landed();
+    barrier();
+    if (!grp_a) copy(p + 1);  // window 2p+2 .. 2p+4
+    softmax(p);
+    if (grp_a) copies_landed();
+    barrier();
+  };
+
+  issue(kbh, 0, K_STAGE0, false);
+  copies_landed();
+  barrier();  // barrier 0
+  if (!grp_a) {
+    copy(0);
+    barrier();  // group B's leading barrier (barrier 1 for group A)
   }
-  tile(t % NSTAGE, Last{}, t);  // the last tile (masked when S is ragged)
+  // period 0: no P V yet
+  if (grp_a) copy(0);
+  mphase(I0{}, I0{}, F{}, T{});
+  if (!grp_a) copies_landed();
+  barrier();
+  if (!grp_a) copy(1);
+  softmax(0);
+  if (grp_a) copies_landed();
+  barrier();
+  int p = 1;
+  for (; p + 1 < n_kt; p += 2) {  // two periods per trip: stage offsets are immediates
+    period(I1{}, p);
+    period(I0{}, p + 1);
+  }
+  if (p < n_kt) {  // p odd
+    period(I1{}, p);
+    ++p;
+  }
+  // M(n_kt): P V of the last tile only
+  if (p & 1) mphase(I0{}, I0{}, T{}, F{});
+  else mphase(I1{}, I0{}, T{}, F{});
+  if (grp_a) barrier();  // matches group B's leading barrier
 
   // ---- epilogue: O = acc / l, BF16, rows < S
+  mfma_drain(acc[0], acc[1], acc[2], acc[3]);
+  const float inv = 1.0f / half_pair_sum(lsum);
+  if (qi < S) {
 #pragma unroll
-  for (int g = 0; g < QG; ++g) mfma_drain(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const float inv = 1.0f / half_pair_sum(lsum[g]);
-    const int i = q0 + 32 * g + ln;
-    if (i < S) {
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = 32 * dt + 8 * rq + 4 * hl;
+        bf16x4 ov;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d = 32 * dt + 8 * rq + 4 * hl;
-          bf16x4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[g][dt][4 * rq + e] * inv);
-          *(bf16x4*)(obh + i * tok + d) = ov;
-        }
-    }
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[dt][4 * rq + e] * inv);
+        *(bf16x4*)(obh + qi * tok + d) = ov;
+      }
   }
 }
 
 }  // namespace bf16attn
 
 // Query rows per workgroup of the launched configuration.
-constexpr int kBf16QG = DITATTN_BF16_QG;
-constexpr int kBf16BQ = bf16attn::NW * kBf16QG * 32;
+constexpr int kBf16BQ = bf16attn::NW * 32;
 
 int bf16_tile_rows() { return kBf16BQ; }
 
@@ -357,7 +385,7 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
                                 int S, int H, float c, hipStream_t stream) {
   const int num_qt = (S + kBf16BQ - 1) / kBf16BQ;
   const int n_tiles = B * H * num_qt;
-  hipLaunchKernelGGL(bf16attn::attn_fwd_bf16_kernel<kBf16QG>, dim3(n_tiles), dim3(bf16attn::NW * 64),
+  hipLaunchKernelGGL(bf16attn::attn_fwd_bf16_kernel, dim3(n_tiles), dim3(bf16attn::NW * 64),
                      0, stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, S,
                      H, c, num_qt, n_tiles);
   return hipGetLastError();

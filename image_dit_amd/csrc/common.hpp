@@ -84,6 +84,19 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET) : "memory");
   return r;
 }
+// ds_read_b128 as inline assembly (see above); `addr` is an LDS byte address.
+template <int OFFSET>
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET) : "memory");
+  return r;
+}
+// Wait until at most N LDS operations are outstanding; a and b depend on the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
 // Wait until at most N LDS operations are outstanding and make the given
 // registers depend on the wait, so no consumer can be scheduled above it.
 template <int N>
@@ -99,6 +112,7 @@ __device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d,
 // it, so IR passes cannot sink the computation to a later use.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 // Let the last MFMAs writing these accumulators retire before any VALU reads
 // them (64 wait states, the full latency of a 16-pass MFMA).  The padding this
