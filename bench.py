@@ -3,7 +3,8 @@
 Default: the BF16 path at the FLUX-1024^2 shape (B=1, H=24, S=4608, D=128),
 attention TFLOPS = 4 * B * H * S^2 * D / time, inputs resident in HBM.
 A step is one attn_fwd_bf16 call; K steps are timed with HIP events recorded
-on the stream the kernel is launched on.  The same line also reports the Sage
+on the stream the kernel is launched on (defaults: 200 warmup steps, then 1000
+timed ones, about a quarter second: long enough for steady clocks).  The same line also reports the Sage
 mode at that shape ("sage" = prepare + attention, "sage_core" = attention on
 prepared tensors), the roofline of the dominant kernel and the CPU oracle's
 throughput on a bounded row sample.
@@ -64,7 +65,7 @@ def time_launches(fn, stream, steps, warmup):
     return start.elapsed_time(end) / steps  # ms per call
 
 
-def cpu_baseline(w, q, k, v, target_s=10.0):
+def cpu_baseline(w, q, k, v, target_s=20.0):
     """The oracle's exact fp64 attention on a bounded sample of query rows."""
     import oracle
     from image_dit_amd import synth
@@ -98,8 +99,8 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="flux1024")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sage", action="store_true", help="time the BF16 path only")
