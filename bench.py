@@ -1,20 +1,29 @@
 """Benchmark of the DiT flash self-attention forward on one MI355X.
 
-Default: the BF16 path at the FLUX-1024^2 shape (B=1, H=24, S=4608, D=128),
-attention TFLOPS = 4 * B * H * S^2 * D / time, inputs resident in HBM.
-A step is one attn_fwd_bf16 call; K steps are timed with HIP events recorded
-on the stream the kernel is launched on (defaults: 200 warmup steps, then 1000
-timed ones, about a quarter second: long enough for steady clocks).  The same line also reports the Sage
-mode at that shape ("sage" = prepare + attention, "sage_core" = attention on
-prepared tensors), the roofline of the dominant kernel and the CPU oracle's
-throughput on a bounded row sample.
+Headline: the BF16 path at the FLUX-1024^2 shape (B=1, H=24, S=4608, D=128),
+attention TFLOPS = 4 * B * H * S^2 * D / time, inputs resident in HBM.  A step
+is one attn_fwd_bf16 call.  W warm-up steps, then exactly K timed steps, timed
+with HIP events recorded on the stream the kernel is launched on; events at the
+quarter marks give the first- and last-quarter ms per step (the clock regime).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+The same JSON line carries one row per (workload, mode) for the DiT shapes:
+  bf16       attn_fwd_bf16                      vs the BF16 MFMA peak
+  sage       sage_prepare + sage_attn_fwd       vs the 8-bit MFMA peak
+  sage_core  sage_attn_fwd on prepared tensors  vs the 8-bit MFMA peak
+  prepare    sage_prepare                       vs the HBM peak (algorithmic bytes)
+Rows are timed before the headline (so the headline runs on a busy, clocked-up
+GPU, stated in the line), each for at least --row-ms milliseconds.  The FLUX-1024
+Sage rows use the K-bias workload of that shape.  Row inputs other than the
+headline's are drawn on the GPU from a seeded generator (same distribution).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--rows all|none|W:M,...]
+    python bench.py --only wan720p:bf16,wan720p:sage_core --reps 3   # profiling runs
     python bench.py --copy-calibration     # plain copy for PMC byte scaling
 """
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -23,9 +32,18 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "int8": 5033.2}  # 256 CU x 2.4 GHz x 4096 / 8192 per clk
+# 256 CU x 2.4 GHz x (4096 BF16 | 8192 FP8/INT8) per CU per clock
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "int8": 5033.2}
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = {"attn_fwd_bf16": ["image_dit_amd/csrc/attn_bf16.hip", "image_dit_amd/csrc/common.hpp"]}
+KERNEL_SOURCES = {
+    "attn_fwd_bf16": ["image_dit_amd/csrc/attn_bf16.hip", "image_dit_amd/csrc/common.hpp"],
+    "sage_attn_fwd": ["image_dit_amd/csrc/attn_sage.hip", "image_dit_amd/csrc/common.hpp"],
+    "sage_prepare": ["image_dit_amd/csrc/prepare.hip", "image_dit_amd/csrc/common.hpp"],
+}
+MODES = ("bf16", "sage", "sage_core", "prepare")
+DEFAULT_ROWS = ["flux1024:sage", "flux1024:sage_core", "flux1024:prepare",
+                "flux2048:bf16", "flux2048:sage", "flux2048:sage_core", "flux2048:prepare",
+                "wan720p:bf16", "wan720p:sage", "wan720p:sage_core", "wan720p:prepare"]
 
 
 def kernel_sha(name):
@@ -50,19 +68,43 @@ def measured_traffic(name, workload):
     return float(m_b.group(1))
 
 
-def time_launches(fn, stream, steps, warmup):
+def timed(fn, stream, steps, warmup, marks=(0.25, 0.75)):
+    """ms per call over `steps` calls after `warmup` untimed ones, plus the ms
+    per call of the first and last quarter of the timed calls."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
+    cut = sorted({0, steps} | {int(round(steps * m)) for m in marks})
+    ev = {i: torch.cuda.Event(enable_timing=True) for i in cut}
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    end.record(stream)
+        if i + 1 in ev:
+            ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms per call
+    total = ev[0].elapsed_time(ev[steps]) / steps
+    q1, q3 = cut[1], cut[-2]
+    first = ev[0].elapsed_time(ev[q1]) / max(q1, 1)
+    last = ev[q3].elapsed_time(ev[steps]) / max(steps - q3, 1)
+    return total, first, last
+
+
+def timed_for(fn, stream, min_ms, min_reps=3):
+    """Time `fn` for at least min_ms milliseconds (after two warm-up calls)."""
+    import torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    est = max(e0.elapsed_time(e1), 1e-3)
+    reps = max(min_reps, int(math.ceil(min_ms / est)))
+    ms, _, _ = timed(fn, stream, reps, 0)
+    return ms, reps
 
 
 def cpu_baseline(w, q, k, v, target_s=20.0):
@@ -96,14 +138,88 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
+class Inputs:
+    """Device inputs and output buffers of one workload, made once."""
+
+    def __init__(self, w, dev, qkv=None):
+        import torch
+        from image_dit_amd import synth
+        self.w = w
+        if qkv is None:
+            qkv = synth.make_qkv_device(w.B, w.S, w.H, dev, w.D, seed=w.seed, k_bias_std=w.k_bias_std)
+        self.q, self.k, self.v = (t.to(dev) for t in qkv)
+        self.out = torch.empty_like(self.q)
+        self._prep = None
+
+    def prepared(self, stream):
+        import image_dit_amd as ia
+        if self._prep is None:
+            self._prep = ia.sage_prepare(self.q, self.k, self.v, self.w.scale, stream=stream)
+        return self._prep
+
+
+def mode_fn(inp, mode, stream):
+    import image_dit_amd as ia
+    w = inp.w
+    if mode == "bf16":
+        return lambda: ia.attn_fwd_bf16(inp.q, inp.k, inp.v, w.scale, out=inp.out, stream=stream)
+    prep = inp.prepared(stream)
+    if mode == "prepare":
+        return lambda: ia.sage_prepare(inp.q, inp.k, inp.v, w.scale, out=prep, stream=stream)
+    if mode == "sage_core":
+        return lambda: ia.sage_attn_fwd(prep, w.S, w.H, w.scale, out=inp.out, stream=stream)
+    if mode == "sage":
+        def f():
+            ia.sage_prepare(inp.q, inp.k, inp.v, w.scale, out=prep, stream=stream)
+            ia.sage_attn_fwd(prep, w.S, w.H, w.scale, out=inp.out, stream=stream)
+        return f
+    raise ValueError(mode)
+
+
+def row_record(w, mode, ms, reps):
+    from image_dit_amd import cost
+    flops = cost.attn_flops(w.B, w.H, w.S, w.D)
+    rec = {"workload": w.name, "mode": mode, "B": w.B, "H": w.H, "S": w.S, "ms": ms, "reps": reps}
+    if mode == "prepare":
+        nbytes = cost.sage_prepare_bytes(w.B, w.H, w.S, w.D)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rec.update(bound="hbm", gbs=gbs, algorithmic_bytes=nbytes, peak=PEAK_HBM_GBS,
+                   frac=gbs / PEAK_HBM_GBS)
+    else:
+        tf = flops / (ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS["bf16" if mode == "bf16" else "int8"]
+        rec.update(bound="mfma", tflops=tf, peak=peak, frac=tf / peak)
+    return rec
+
+
+def parse_rows(spec):
+    from image_dit_amd import synth
+    if spec in ("", "none"):
+        return []
+    items = DEFAULT_ROWS if spec == "all" else [x for x in spec.split(",") if x]
+    out = []
+    for it in items:
+        wname, mode = it.split(":")
+        if mode not in MODES:
+            raise SystemExit("unknown mode %r (one of %s)" % (mode, ", ".join(MODES)))
+        if wname == "flux1024" and mode != "bf16":
+            wname = "flux1024_kbias"  # the Sage configuration of this shape carries the K bias
+        if wname not in synth.WORKLOADS:
+            raise SystemExit("unknown workload %r" % wname)
+        out.append((wname, mode))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="flux1024")
+    ap.add_argument("--rows", default="all", help="per-config rows: all, none or workload:mode,...")
+    ap.add_argument("--row-ms", type=float, default=200.0, help="minimum timed ms per row")
+    ap.add_argument("--only", default="", help="run only these rows, --reps calls each (profiling)")
+    ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-sage", action="store_true", help="time the BF16 path only")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -121,49 +237,47 @@ def main():
         copy_calibration()
         return
 
-    w = synth.WORKLOADS[args.workload]
-    q, k, v = synth.workload_qkv(w)
+    ia.load()
     dev = torch.device("cuda", 0)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    out = torch.empty_like(qd)
     stream = torch.cuda.Stream()
+    inputs = {}
+
+    def get_inputs(name, qkv=None):
+        if name not in inputs:
+            inputs[name] = Inputs(synth.WORKLOADS[name], dev, qkv)
+        return inputs[name]
+
+    if args.only:
+        for wname, mode in parse_rows(args.only):
+            inp = get_inputs(wname)
+            fn = mode_fn(inp, mode, stream)
+            ms, _, _ = timed(fn, stream, args.reps, 1)
+            print(json.dumps(row_record(inp.w, mode, ms, args.reps)), flush=True)
+            inputs.clear()
+            torch.cuda.empty_cache()
+        return
+
+    # ---- per-config rows (time-sized), largest workload last so memory is freed in between
+    rows = []
+    for wname, mode in parse_rows(args.rows):
+        if wname not in inputs:
+            inputs.clear()
+            torch.cuda.empty_cache()
+        inp = get_inputs(wname)
+        ms, reps = timed_for(mode_fn(inp, mode, stream), stream, args.row_ms)
+        rows.append(row_record(inp.w, mode, ms, reps))
+    inputs.clear()
+    torch.cuda.empty_cache()
+
+    # ---- headline: FLUX-1024 BF16, exactly W warm-up + K timed steps
+    w = synth.WORKLOADS["flux1024"]
+    q, k, v = synth.workload_qkv(w)
+    inp = get_inputs("flux1024", (q, k, v))
+    ms, first, last = timed(mode_fn(inp, "bf16", stream), stream, args.steps, args.warmup)
     flops = cost.attn_flops(w.B, w.H, w.S, w.D)
-
-    def bf16_step():
-        ia.attn_fwd_bf16(qd, kd, vd, w.scale, out=out, stream=stream)
-
-    ms = time_launches(bf16_step, stream, args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
+    rows.insert(0, dict(row_record(w, "bf16", ms, args.steps), headline=True))
 
-    modes = {}
-    if not args.no_sage:
-        prepared = ia.sage_prepare(qd, kd, vd, w.scale, stream=stream)
-        sout = torch.empty_like(qd)
-
-        def prep_step():
-            ia.sage_prepare(qd, kd, vd, w.scale, out=prepared, stream=stream)
-
-        def core_step():
-            ia.sage_attn_fwd(prepared, w.S, w.H, w.scale, out=sout, stream=stream)
-
-        def sage_step():
-            prep_step()
-            core_step()
-
-        ms_prep = time_launches(prep_step, stream, args.steps, args.warmup)
-        ms_core = time_launches(core_step, stream, args.steps, args.warmup)
-        ms_sage = time_launches(sage_step, stream, args.steps, args.warmup)
-        peak8 = PEAK_TFLOPS["int8"]
-        modes = {
-            "sage": {"ms": ms_sage, "tflops": flops / (ms_sage * 1e-3) / 1e12},
-            "sage_core": {"ms": ms_core, "tflops": flops / (ms_core * 1e-3) / 1e12,
-                          "frac_of_8bit_peak": flops / (ms_core * 1e-3) / 1e12 / peak8},
-            "sage_prepare": {"ms": ms_prep,
-                             "gbs": cost.sage_prepare_bytes(w.B, w.H, w.S, w.D) / (ms_prep * 1e-3) / 1e9,
-                             "frac_of_hbm_peak": cost.sage_prepare_bytes(w.B, w.H, w.S, w.D) / (ms_prep * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        }
-
-    traffic = measured_traffic("attn_fwd_bf16", w.name)
     line = {
         "metric": "attention TFLOPS (4*B*H*S^2*D/s) at FLUX/Wan DiT shapes; % of MFMA peak",
         "value": tflops,
@@ -177,14 +291,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded randn BF16 Q/K/V)",
-        "config": {"workload": "%s self-attention, BF16 path" % w.name, "B": w.B, "H": w.H, "S": w.S,
+        "config": {"workload": "flux1024 self-attention, BF16 path", "B": w.B, "H": w.H, "S": w.S,
                    "D": w.D, "causal": False},
+        "clock_regime": {"first_quarter_ms_per_step": first, "last_quarter_ms_per_step": last,
+                         "timed_after": "%d per-config rows (%.1f s of GPU work)"
+                                        % (len(rows) - 1, sum(r["ms"] * (r["reps"] + 3) for r in rows[1:]) / 1e3)},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": tflops / PEAK_TFLOPS["bf16"],
-                     "traffic": traffic,
+                     "traffic": measured_traffic("attn_fwd_bf16", w.name),
                      "kernel": "attn_fwd_bf16_kernel", "algorithmic_flop_per_launch": flops,
                      "algorithmic_bytes_per_launch": cost.attn_bytes_bf16(w.B, w.H, w.S, w.D)},
-        "modes": modes,
+        "rows": rows,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v)

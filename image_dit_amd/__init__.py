@@ -80,6 +80,17 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(tensors, stream):
+    """Tell the caching allocator that `stream` uses tensors this module
+    allocated on the current stream, so it does not hand their memory out
+    again before the work enqueued on `stream` has finished."""
+    import torch
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        t.record_stream(stream)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
@@ -92,6 +103,29 @@ def _check_bshd(name, t, dtype):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+
+
+def _check_out(name, t, shape, dtype, device):
+    """Full check of a caller-supplied output: the library cannot see buffer
+    sizes, so a short buffer would be written past its end."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device != device:
+        raise ValueError("%s must be a tensor on %s" % (name, device))
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _prepared_specs(B, S, H, D):
+    """(name, shape, dtype) of the six tensors sage_prepare writes."""
+    import torch
+    Sp = sage_padded_len(S)
+    return (("q_i8", (B, H, Sp, D), torch.int8), ("q_scale", (B, H, Sp // 32), torch.float32),
+            ("k_i8", (B, H, Sp, D), torch.int8), ("k_scale", (B, H, Sp // 32), torch.float32),
+            ("v_fp8", (B, H, D, Sp), torch.uint8), ("v_scale", (B, H, D), torch.float32))
 
 
 def _dims(q):
@@ -111,8 +145,9 @@ def attn_fwd_bf16(q, k, v, scale, out=None, stream=None):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S, H, D)))
     if out is None:
         out = torch.empty_like(q)
+        _on_stream([out], stream)
     else:
-        _check_bshd("out", out, torch.bfloat16)
+        _check_out("out", out, (B, S, H, D), torch.bfloat16, q.device)
     st = lib.attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, H, D, float(scale),
                            _stream_handle(stream))
     _status(lib, "attn_fwd_bf16", st)
@@ -133,15 +168,15 @@ def sage_prepare(q, k, v, scale, out=None, stream=None):
         _check_bshd(name, t, torch.bfloat16)
         if tuple(t.shape) != (B, S, H, D):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S, H, D)))
+    specs = _prepared_specs(B, S, H, D)
     if out is None:
-        Sp = sage_padded_len(S)
-        dev = q.device
-        out = (torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
-               torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
-               torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev),
-               torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev),
-               torch.empty((B, H, D, Sp), dtype=torch.uint8, device=dev),
-               torch.empty((B, H, D), dtype=torch.float32, device=dev))
+        out = tuple(torch.empty(shape, dtype=dt, device=q.device) for _, shape, dt in specs)
+        _on_stream(out, stream)
+    else:
+        if len(out) != 6:
+            raise ValueError("out must be the 6 tensors of a sage_prepare result")
+        for t, (name, shape, dt) in zip(out, specs):
+            _check_out(name, t, shape, dt, q.device)
     st = lib.sage_prepare(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S, H, D,
                           float(scale), _stream_handle(stream))
     _status(lib, "sage_prepare", st)
@@ -152,25 +187,19 @@ def sage_attn_fwd(prepared, S, H, scale, out=None, stream=None):
     """The Sage forward on the tensors returned by sage_prepare; output [B, S, H, 128] BF16."""
     import torch
     lib = load()
-    q_i8 = prepared[0]
-    B = int(q_i8.shape[0])
-    D = int(q_i8.shape[3])
-    if out is None:
-        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q_i8.device)
-    else:
-        _check_bshd("out", out, torch.bfloat16)
     if len(prepared) != 6:
         raise ValueError("expected the 6 tensors returned by sage_prepare")
-    Sp = sage_padded_len(S)
-    expect = ((B, H, Sp, D, torch.int8), (B, H, Sp // 32, torch.float32),
-              (B, H, Sp, D, torch.int8), (B, H, Sp // 32, torch.float32),
-              (B, H, D, Sp, torch.uint8), (B, H, D, torch.float32))
-    for t, e in zip(prepared, expect):
-        if tuple(t.shape) != e[:-1] or t.dtype != e[-1]:
-            raise ValueError("prepared tensor %s/%s does not match S=%d, H=%d (expected %s/%s)"
-                             % (tuple(t.shape), t.dtype, S, H, e[:-1], e[-1]))
-        if not t.is_contiguous() or t.device.type != "cuda":
-            raise ValueError("prepared tensors must be contiguous GPU tensors")
+    q_i8 = prepared[0]
+    if not isinstance(q_i8, torch.Tensor) or q_i8.dim() != 4 or q_i8.device.type != "cuda":
+        raise ValueError("prepared tensors must be the GPU tensors returned by sage_prepare")
+    B, D = int(q_i8.shape[0]), int(q_i8.shape[3])
+    for t, (name, shape, dt) in zip(prepared, _prepared_specs(B, int(S), int(H), D)):
+        _check_out(name, t, shape, dt, q_i8.device)
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q_i8.device)
+        _on_stream([out], stream)
+    else:
+        _check_out("out", out, (B, S, H, D), torch.bfloat16, q_i8.device)
     st = lib.sage_attn_fwd(*[_ptr(t) for t in prepared], _ptr(out), B, int(S), int(H), D,
                            float(scale), _stream_handle(stream))
     _status(lib, "sage_attn_fwd", st)

@@ -20,18 +20,20 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 }
 
 // Shared shape checks.  On success *elems = B * S * H * 128 and *s_pad = S_pad.
+// The bounds are the ranges the kernels index in:
+//   * B * H * S_pad <= INT32_MAX: tile, block and grid indices are int, and
+//     every grid times its workgroup size stays below 2^32 work-items;
+//   * H <= DITATTN_MAX_HEADS: the BF16 kernel addresses a K/V tile row as a
+//     32-bit byte offset r * H * 256 with r < 64 (63 * 65536 * 256 < 2^32).
 int check_shape(int B, int S, int H, int D, float scale, int64_t* elems, int* s_pad) {
   if (B < 1 || S < 1 || H < 1) return DITATTN_EINVAL;
   if (!isfinite(scale) || !(scale > 0.0f)) return DITATTN_EINVAL;
   if (D != 128) return DITATTN_EUNSUPPORTED;
-  // Kernels index tokens with int and elements with int64; the padded length,
-  // tile counts and grid must stay below 2^31.
+  if (H > DITATTN_MAX_HEADS) return DITATTN_EOVERFLOW;
   if (S > (INT32_MAX - 255)) return DITATTN_EOVERFLOW;
   const int64_t sp = (static_cast<int64_t>(S) + 255) / 256 * 256;
-  const int64_t bh = static_cast<int64_t>(B) * H;
-  if (bh > INT32_MAX) return DITATTN_EOVERFLOW;
-  const int64_t e = bh * sp * 128;  // <= 2^31 * 2^31 * 2^7: fits int64
-  if (e > INT64_MAX / 4 / sp || bh * sp > INT32_MAX) return DITATTN_EOVERFLOW;
+  const int64_t bh = static_cast<int64_t>(B) * H;  // < 2^31 * 2^16: no int64 overflow
+  if (bh * sp > INT32_MAX) return DITATTN_EOVERFLOW;
   *elems = bh * S * 128;
   *s_pad = static_cast<int>(sp);
   return DITATTN_OK;
@@ -62,6 +64,19 @@ int ditattn_sage_padded_len(int S) {
   return (S + 255) / 256 * 256;
 }
 
+int ditattn_check_shape(int entry, int B, int S, int H, int D, float scale) {
+  int64_t elems;
+  int s_pad;
+  int st = check_shape(B, S, H, D, scale, &elems, &s_pad);
+  if (st != DITATTN_OK) return st;
+  switch (entry) {
+    case DITATTN_ENTRY_ATTN_FWD_BF16:
+    case DITATTN_ENTRY_SAGE_PREPARE: return DITATTN_OK;
+    case DITATTN_ENTRY_SAGE_ATTN_FWD: return S > DITATTN_MAX_SEQ_SAGE ? DITATTN_EOVERFLOW : DITATTN_OK;
+    default: return DITATTN_EINVAL;
+  }
+}
+
 int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, int S, int H,
                   int D, float scale, hipStream_t stream) {
   int64_t elems;
@@ -73,8 +88,6 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, i
   const int64_t bytes = elems * 2;
   if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
     return DITATTN_EINVAL;
-  const int64_t tiles = static_cast<int64_t>(B) * H * ((S + ditattn::bf16_tile_rows() - 1) / ditattn::bf16_tile_rows());
-  if (tiles > INT32_MAX) return DITATTN_EOVERFLOW;
   if (ditattn::launch_attn_fwd_bf16(q, k, v, o, B, S, H, log2e_scale(scale), stream) != hipSuccess)
     return DITATTN_EHIP;
   return DITATTN_OK;
@@ -119,6 +132,8 @@ int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
   int s_pad;
   int st = check_shape(B, S, H, D, scale, &elems, &s_pad);
   if (st != DITATTN_OK) return st;
+  // the kernel addresses a V^T tile row as a 32-bit byte offset c * S_pad, c < 128
+  if (S > DITATTN_MAX_SEQ_SAGE) return DITATTN_EOVERFLOW;
   const void* ptrs[7] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o};
   for (const void* p : ptrs)
     if (!p) return DITATTN_EINVAL;
@@ -132,8 +147,6 @@ int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
   const int64_t in_bytes[6] = {code_bytes, qk_scale_bytes, code_bytes, qk_scale_bytes, code_bytes, v_scale_bytes};
   for (int i = 0; i < 6; ++i)
     if (overlaps(o, elems * 2, ins[i], in_bytes[i])) return DITATTN_EINVAL;
-  const int64_t tiles = bh * ((S + ditattn::sage_tile_rows() - 1) / ditattn::sage_tile_rows());
-  if (tiles > INT32_MAX) return DITATTN_EOVERFLOW;
   if (ditattn::launch_sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S, H,
                                     s_pad, stream) != hipSuccess)
     return DITATTN_EHIP;

@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace ditattn {
 namespace bf16attn {
@@ -379,16 +380,13 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // Query rows per workgroup of the launched configuration.
 constexpr int kBf16BQ = bf16attn::NW * 32;
 
-int bf16_tile_rows() { return kBf16BQ; }
-
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B,
                                 int S, int H, float c, hipStream_t stream) {
   const int num_qt = (S + kBf16BQ - 1) / kBf16BQ;
   const int n_tiles = B * H * num_qt;
-  hipLaunchKernelGGL(bf16attn::attn_fwd_bf16_kernel, dim3(n_tiles), dim3(bf16attn::NW * 64),
-                     0, stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, S,
-                     H, c, num_qt, n_tiles);
-  return hipGetLastError();
+  return launch(bf16attn::attn_fwd_bf16_kernel, dim3(n_tiles), dim3(bf16attn::NW * 64), stream,
+                (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, S, H, c, num_qt,
+                n_tiles);
 }
 
 }  // namespace ditattn

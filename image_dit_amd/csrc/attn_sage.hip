@@ -258,17 +258,14 @@ sage_attn_fwd_kernel(const int8_t* __restrict__ q_i8, const float* __restrict__ 
 
 }  // namespace sageattn
 
-int sage_tile_rows() { return sageattn::BQ; }
-
 hipError_t launch_sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                 const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
                                 void* o, int B, int S, int H, int S_pad, hipStream_t stream) {
   const int num_qt = (S + sageattn::BQ - 1) / sageattn::BQ;
   const int n_tiles = B * H * num_qt;
-  hipLaunchKernelGGL(sageattn::sage_attn_fwd_kernel, dim3(n_tiles), dim3(sageattn::NW * 64), 0, stream,
-                     q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, (__bf16*)o, S, H, S_pad, num_qt,
-                     n_tiles);
-  return hipGetLastError();
+  return launch(sageattn::sage_attn_fwd_kernel, dim3(n_tiles), dim3(sageattn::NW * 64), stream,
+                q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, (__bf16*)o, S, H, S_pad, num_qt,
+                n_tiles);
 }
 
 }  // namespace ditattn

@@ -36,13 +36,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
-// Value of `x` held by lane l ^ 32 (the other half of the wavefront).
-__device__ __forceinline__ float other_half(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  // lanes 0..31 receive the upper half's value in r[1], lanes 32..63 the lower half's in r[0]
-  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
-}
-
 // max / sum of x over lanes l and l ^ 32.
 __device__ __forceinline__ float half_pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

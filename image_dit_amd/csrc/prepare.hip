@@ -15,11 +15,18 @@
 //   v_absmax   per (b, token range, 512 channels): running |v| maxima in
 //              registers, combined across the 4 waves in LDS, then one
 //              atomicMax per channel on the fp32 bit pattern (order free: max
-//              of non-negative floats = max of their bit patterns).  The
-//              accumulator is cleared by quant_qk, which runs first.
+//              of non-negative floats = max of their bit patterns).
 //   v_quant    per (b, h, 128-token chunk): quantize, transpose through LDS,
-//              write 128 channel rows of 128 B.
-//   v_finalize v_scale = absmax / 448 in place.
+//              write 128 channel rows of 128 B; the chunk-0 workgroup of each
+//              (b, h) also writes the final v_scale = absmax / 448.
+// The V absmax accumulator is the v_scale buffer itself.  While it holds a
+// running maximum, bit 31 of each word is set (quant_qk, which runs first,
+// initializes it to 0x80000000, i.e. a maximum of +0 with the flag); the
+// finished scale absmax / 448 is a non-negative float, bit 31 clear.  A
+// v_quant workgroup that reads a word of its (b, h) either finds the flagged
+// maximum and divides it by 448 itself or finds the finished scale written by
+// the chunk-0 workgroup: both give the same value, so the write needs no
+// ordering against the other workgroups' reads and no fourth launch.
 // Division and rounding are IEEE fp32 (the library is built with correctly
 // rounded division), so the codes are bit-identical to a scalar CPU quantizer.
 #include "common.hpp"
@@ -27,6 +34,8 @@
 
 namespace ditattn {
 namespace prep {
+
+constexpr uint32_t kAmaxFlag = 0x80000000u;  // bit 31 marks a running absmax word
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -43,9 +52,12 @@ quant_qk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 int8_t* __restrict__ q_i8, float* __restrict__ q_scale, int8_t* __restrict__ k_i8,
                 float* __restrict__ k_scale, int S, int H, int nblk, int units, float c,
                 uint32_t* __restrict__ amax_bits, int n_amax) {
-  // clear the V absmax accumulator for v_absmax_kernel, which runs next on the stream
-  for (int i = (blockIdx.y * gridDim.x + blockIdx.x) * 256 + threadIdx.x; i < n_amax; i += gridDim.x * gridDim.y * 256)
-    amax_bits[i] = 0u;
+  // initialize the V absmax accumulator (flagged +0) for v_absmax_kernel, which runs
+  // next on the stream; the first ceil(n_amax / 256) workgroups of the Q half do it
+  {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (blockIdx.y == 0 && i < n_amax) amax_bits[i] = kAmaxFlag;
+  }
 
   const bool is_q = blockIdx.y == 0;
   const uint16_t* x = is_q ? q : k;
@@ -101,20 +113,23 @@ quant_qk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 // ---------------------------------------------------------------- V absmax
-// grid (ceil(S / tok_per_wg), ceil(H * 16 / 64), B), 256 threads.  Thread t owns
-// chunk column blockIdx.y * 64 + (t & 63) (8 channels) and tokens
+// grid: B * colblk * nchunk workgroups of 256 threads (nchunk = ceil(S / tok_per_wg),
+// colblk = ceil(H * 16 / 64)), workgroup x = (b * colblk + cb) * nchunk + chunk.
+// Thread t owns chunk column cb * 64 + (t & 63) (8 channels) and tokens
 // j0 + (t >> 6) + 4 k: a wave reads 1 KB of one token row.  The 4 waves combine
 // their maxima in LDS, then one atomicMax per channel on the fp32 bit pattern
-// of |v|.  amax_bits: [B, H, 128], cleared by quant_qk_kernel, which runs first.
+// of |v|.  amax_bits: [B, H, 128], initialized by quant_qk_kernel, which runs first.
 __global__ void __launch_bounds__(256)
 v_absmax_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits, int S, int H,
-                int tok_per_wg) {
+                int tok_per_wg, int nchunk, int colblk) {
   __shared__ uint32_t red[4][64][8];
-  const int b = blockIdx.z;
+  const int chunk = blockIdx.x % nchunk;
+  const int bc = blockIdx.x / nchunk;
+  const int b = bc / colblk, cb = bc - b * colblk;
   const int ncol = H * 16;  // 16-byte chunks per token row (all heads)
-  const int col = blockIdx.y * 64 + (threadIdx.x & 63);
+  const int col = cb * 64 + (threadIdx.x & 63);
   const int wv = threadIdx.x >> 6;
-  const int j0 = blockIdx.x * tok_per_wg;
+  const int j0 = chunk * tok_per_wg;
   const int j1 = min(j0 + tok_per_wg, S);
   const int64_t tok = (int64_t)H * kHeadDim;
   uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // |v| as bf16 magnitude bits
@@ -144,9 +159,9 @@ v_absmax_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits
     const int idx = threadIdx.x + 256 * k;
     const int c = idx >> 3, e = idx & 7;
     const uint32_t m4 = max(max(red[0][c][e], red[1][c][e]), max(red[2][c][e], red[3][c][e]));
-    const int gcol = blockIdx.y * 64 + c;
+    const int gcol = cb * 64 + c;
     // bf16 magnitude bits << 16 = fp32 bits of |v|; finite magnitudes order like integers
-    if (gcol < ncol && m4 != 0u) atomicMax(amax_bits + (int64_t)b * H * kHeadDim + 8 * gcol + e, m4 << 16);
+    if (gcol < ncol && m4 != 0u) atomicMax(amax_bits + (int64_t)b * H * kHeadDim + 8 * gcol + e, (m4 << 16) | kAmaxFlag);
   }
 }
 
@@ -154,21 +169,28 @@ v_absmax_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits
 constexpr int kVTok = 128;          // tokens per v_quant workgroup
 constexpr int kVRowB = kVTok + 8;   // LDS row stride in bytes (channel rows)
 
-// grid (S_pad / kVTok, B * H).  Thread t: chunk t & 15 (8 channels), tokens 8 * (t >> 4) + 0..7.
+// grid: B * H * (S_pad / kVTok) workgroups, x = bh * (S_pad / kVTok) + token chunk.
+// Thread t: chunk t & 15 (8 channels), tokens 8 * (t >> 4) + 0..7.
+// amax_bits doubles as the v_scale output (see the top of this file).
 __global__ void __launch_bounds__(256)
-v_quant_kernel(const uint16_t* __restrict__ v, const uint32_t* __restrict__ amax_bits,
+v_quant_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits,
                uint8_t* __restrict__ v_fp8, int S, int H, int S_pad) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kHeadDim * kVRowB];
-  const int bh = blockIdx.y;
+  const int nch = S_pad / kVTok;
+  const int bh = blockIdx.x / nch;
+  const int tchunk = blockIdx.x - bh * nch;
   const int b = bh / H, h = bh - b * H;
-  const int j0 = blockIdx.x * kVTok;
+  const int j0 = tchunk * kVTok;
   const int chunk = threadIdx.x & 15, tg = threadIdx.x >> 4;
   const int64_t tok = (int64_t)H * kHeadDim;
   const uint16_t* src = v + ((int64_t)b * S * H + h) * kHeadDim;
 
   float sv[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sv[e] = __uint_as_float(amax_bits[(int64_t)bh * kHeadDim + 8 * chunk + e]) / 448.0f;
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w = amax_bits[(int64_t)bh * kHeadDim + 8 * chunk + e];
+    sv[e] = (w & kAmaxFlag) ? __uint_as_float(w & ~kAmaxFlag) / 448.0f : __uint_as_float(w);
+  }
 
   float x[8][8];  // [token][channel]
 #pragma unroll
@@ -201,6 +223,11 @@ v_quant_kernel(const uint16_t* __restrict__ v, const uint32_t* __restrict__ amax
     *(uint2*)(lds + (8 * chunk + e) * kVRowB + 8 * tg) = uint2{word[0], word[1]};
   }
   __syncthreads();
+  // the chunk-0 workgroup publishes the finished scales (threads 0..15 own all 128 channels)
+  if (tchunk == 0 && threadIdx.x < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax_bits[(int64_t)bh * kHeadDim + 8 * chunk + e] = __float_as_uint(sv[e]);
+  }
   // 128 channel rows x 128 B; 8 bytes per thread per step, 16 threads per row
   uint8_t* dst = v_fp8 + (int64_t)bh * kHeadDim * S_pad + j0;
 #pragma unroll
@@ -211,12 +238,6 @@ v_quant_kernel(const uint16_t* __restrict__ v, const uint32_t* __restrict__ amax
   }
 }
 
-__global__ void __launch_bounds__(256)
-v_finalize_kernel(float* __restrict__ v_scale, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) v_scale[i] = v_scale[i] / 448.0f;  // absmax bits read as fp32
-}
-
 }  // namespace prep
 
 hipError_t launch_sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8,
@@ -225,22 +246,23 @@ hipError_t launch_sage_prepare(const void* q, const void* k, const void* v, int8
                                hipStream_t stream) {
   const int nblk = S_pad / 32;
   const int units = B * H * nblk;
-  const int nscale = B * H * kHeadDim;
+  const int nscale = B * H * kHeadDim;  // <= units: the Q half of quant_qk covers it
   uint32_t* amax_bits = reinterpret_cast<uint32_t*>(v_scale);
-  hipLaunchKernelGGL(prep::quant_qk_kernel, dim3((units + 3) / 4, 2), dim3(256), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, q_i8, q_scale, k_i8, k_scale, S, H, nblk,
-                     units, c, amax_bits, nscale);
+  hipError_t e = launch(prep::quant_qk_kernel, dim3((units + 3) / 4, 2), dim3(256), stream,
+                        (const uint16_t*)q, (const uint16_t*)k, q_i8, q_scale, k_i8, k_scale, S, H,
+                        nblk, units, c, amax_bits, nscale);
+  if (e != hipSuccess) return e;
   // V absmax: about 1000 workgroups whatever the shape, token ranges a multiple of 16
   const int colblk = (H * 16 + 63) / 64;
   int tok_per_wg = (int)(((int64_t)S * colblk * B + 1023) / 1024);
   tok_per_wg = (tok_per_wg + 15) / 16 * 16;
   if (tok_per_wg < 16) tok_per_wg = 16;
-  hipLaunchKernelGGL(prep::v_absmax_kernel, dim3((S + tok_per_wg - 1) / tok_per_wg, colblk, B), dim3(256), 0,
-                     stream, (const uint16_t*)v, amax_bits, S, H, tok_per_wg);
-  hipLaunchKernelGGL(prep::v_quant_kernel, dim3(S_pad / prep::kVTok, B * H), dim3(256), 0, stream,
-                     (const uint16_t*)v, (const uint32_t*)amax_bits, v_fp8, S, H, S_pad);
-  hipLaunchKernelGGL(prep::v_finalize_kernel, dim3((nscale + 255) / 256), dim3(256), 0, stream, v_scale, nscale);
-  return hipGetLastError();
+  const int nchunk = (S + tok_per_wg - 1) / tok_per_wg;
+  e = launch(prep::v_absmax_kernel, dim3(B * colblk * nchunk), dim3(256), stream, (const uint16_t*)v,
+             amax_bits, S, H, tok_per_wg, nchunk, colblk);
+  if (e != hipSuccess) return e;
+  return launch(prep::v_quant_kernel, dim3(B * H * (S_pad / prep::kVTok)), dim3(256), stream,
+                (const uint16_t*)v, amax_bits, v_fp8, S, H, S_pad);
 }
 
 }  // namespace ditattn

@@ -68,6 +68,20 @@ def make_qkv(B, S, H, D=HEAD_DIM, seed=0, k_bias_std=0.0):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def make_qkv_device(B, S, H, device, D=HEAD_DIM, seed=0, k_bias_std=0.0):
+    """Same distribution as make_qkv, drawn on the GPU from a seeded device
+    generator (fast at the video shapes).  The values differ from make_qkv's;
+    the benchmark uses these only where no oracle comparison is made."""
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    q = torch.randn((B, S, H, D), generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+    k = torch.randn((B, S, H, D), generator=g, dtype=torch.float32, device=device)
+    v = torch.randn((B, S, H, D), generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+    if k_bias_std:
+        bias = float(k_bias_std) * torch.randn((H, D), generator=g, dtype=torch.float32, device=device)
+        k += bias
+    return q, k.to(torch.bfloat16), v
+
+
 def workload_qkv(w: Workload):
     return make_qkv(w.B, w.S, w.H, w.D, seed=w.seed, k_bias_std=w.k_bias_std)
 

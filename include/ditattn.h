@@ -26,8 +26,10 @@
  *     allocates nothing, keeps no state between calls and is thread-safe.
  *   - Tensors are contiguous.  BF16 tensors q, k, v, o are [B, S, H, D]
  *     (token-major, head next, channel fastest), 2 bytes per element.
- *   - D must be 128.  B, S, H must be >= 1 and every byte size must fit in
- *     int64 and the grid limits.
+ *   - D must be 128.  B, S, H must be >= 1.  Size limits (larger shapes
+ *     return DITATTN_EOVERFLOW before anything is enqueued):
+ *       H <= DITATTN_MAX_HEADS, B * H * S_pad <= INT32_MAX, and for
+ *       sage_attn_fwd also S <= DITATTN_MAX_SEQ_SAGE.
  *   - Every pointer must be 16-byte aligned.
  *   - Each call only enqueues work on `stream` (0 = the null stream) and
  *     returns; results are valid once the stream has reached that point.
@@ -54,6 +56,10 @@ typedef struct ihipStream_t* hipStream_t;
 
 #define DITATTN_ABI_VERSION 1
 
+/* Size limits (see the conventions above). */
+#define DITATTN_MAX_HEADS 65536
+#define DITATTN_MAX_SEQ_SAGE (1 << 25)
+
 /* Status codes. */
 #define DITATTN_OK 0
 #define DITATTN_EINVAL (-1)       /* B, S or H < 1, null pointer, scale not finite or <= 0, output aliasing an input */
@@ -71,6 +77,16 @@ const char* ditattn_status_string(int status);
 /* S rounded up to a multiple of 256 (the token length of prepared tensors);
  * -1 if S < 1 or the result overflows int. */
 int ditattn_sage_padded_len(int S);
+
+/* Entry points, for ditattn_check_shape. */
+#define DITATTN_ENTRY_ATTN_FWD_BF16 0
+#define DITATTN_ENTRY_SAGE_PREPARE 1
+#define DITATTN_ENTRY_SAGE_ATTN_FWD 2
+
+/* The status the given entry point returns for these sizes and scale before
+ * it looks at any pointer (DITATTN_OK, DITATTN_EINVAL, DITATTN_EUNSUPPORTED or
+ * DITATTN_EOVERFLOW); DITATTN_EINVAL for an unknown entry.  Touches no GPU. */
+int ditattn_check_shape(int entry, int B, int S, int H, int D, float scale);
 
 /*
  * attn_fwd_bf16 -- o = softmax(q k^T * scale) v per (batch, head), non-causal.

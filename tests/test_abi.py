@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd_bf16", "sage_prepare", "sage_attn_fwd", "ditattn_sage_padded_len",
-              "ditattn_status_string", "ditattn_abi_version"):
+              "ditattn_status_string", "ditattn_abi_version", "ditattn_check_shape"):
         assert n in names
 
 
@@ -130,3 +130,99 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+# ---------------------------------------------------------------- size limits
+# Every accepted shape must be one the kernels index without 32-bit wrap-around:
+# the BF16 kernel forms K/V row offsets r * H * 256 (r < 64) in 32 bits, the Sage
+# kernel forms V^T row offsets c * S_pad (c < 128) in 32 bits, and tile/grid
+# indices are int (B * H * S_pad <= INT32_MAX).  Only the host checks run here.
+ENTRY_BF16, ENTRY_PREP, ENTRY_SAGE = 0, 1, 2
+MAX_HEADS, MAX_SEQ_SAGE = 65536, 1 << 25
+
+
+def check_shape(lib, entry, B, S, H, D=128, scale=0.088):
+    lib.ditattn_check_shape.argtypes = [ctypes.c_int] * 5 + [ctypes.c_float]
+    return lib.ditattn_check_shape(entry, B, S, H, D, scale)
+
+
+def test_limits_are_in_kernel_index_range():
+    # the arithmetic the bounds rest on
+    assert 63 * MAX_HEADS * 256 + 16 * 15 < 2 ** 32
+    assert 63 * (MAX_HEADS + 1) * 256 < 2 ** 32  # H itself is bounded more tightly than needed
+    assert 127 * MAX_SEQ_SAGE + 16 * 3 < 2 ** 32 and MAX_SEQ_SAGE % 256 == 0
+    assert 127 * (MAX_SEQ_SAGE + 256) >= 2 ** 32 - 2 ** 26  # next padded length is close to the wrap
+
+
+@pytest.mark.parametrize("entry", [ENTRY_BF16, ENTRY_PREP, ENTRY_SAGE])
+def test_heads_limit(lib, entry):
+    assert check_shape(lib, entry, 1, 256, MAX_HEADS) == 0
+    assert check_shape(lib, entry, 1, 256, MAX_HEADS + 1) == EOVERFLOW
+
+
+@pytest.mark.parametrize("entry", [ENTRY_BF16, ENTRY_PREP, ENTRY_SAGE])
+def test_total_rows_limit(lib, entry):
+    # B * H * S_pad <= INT32_MAX: 8192 * 261888 fits, 8192 * 262144 = 2^31 does not
+    assert check_shape(lib, entry, 1, 261888, 8192) == 0
+    assert check_shape(lib, entry, 1, 261889, 8192) == EOVERFLOW
+    assert check_shape(lib, entry, 2, 130816, 8192) == 0  # 2 * 8192 * 130816 < 2^31
+    assert check_shape(lib, entry, 2, 130817, 8192) == EOVERFLOW  # S_pad 131072
+
+
+def test_sage_sequence_limit(lib):
+    assert check_shape(lib, ENTRY_SAGE, 1, MAX_SEQ_SAGE, 1) == 0
+    assert check_shape(lib, ENTRY_SAGE, 1, MAX_SEQ_SAGE + 1, 1) == EOVERFLOW
+    # the prepare stage and the BF16 path index nothing in units of S_pad * 128
+    assert check_shape(lib, ENTRY_PREP, 1, MAX_SEQ_SAGE + 1, 1) == 0
+    assert check_shape(lib, ENTRY_BF16, 1, MAX_SEQ_SAGE + 1, 1) == 0
+    # and the entry point itself rejects before looking at pointers
+    assert attn_call(lib, S=MAX_SEQ_SAGE + 1) == EOVERFLOW
+    assert bf16_call(lib, H=MAX_HEADS + 1) == EOVERFLOW
+    assert prep_call(lib, H=MAX_HEADS + 1) == EOVERFLOW
+
+
+def test_check_shape_matches_argument_rules(lib):
+    assert check_shape(lib, ENTRY_BF16, 0, 64, 2) == EINVAL
+    assert check_shape(lib, ENTRY_BF16, 1, 64, 2, D=64) == EUNSUPPORTED
+    assert check_shape(lib, ENTRY_BF16, 1, 64, 2, scale=float("nan")) == EINVAL
+    assert check_shape(lib, 7, 1, 64, 2) == EINVAL
+
+
+# ---------------------------------------------------------------- binding output checks
+def test_binding_rejects_wrong_outputs_before_any_call(monkeypatch):
+    import torch
+    mod = ia
+    calls = []
+
+    class FakeLib:
+        def __getattr__(self, name):
+            def f(*a):
+                calls.append(name)
+                return 0
+            return f
+
+        def ditattn_sage_padded_len(self, S):
+            return (S + 255) // 256 * 256
+
+    monkeypatch.setattr(mod, "load", lambda path=None: FakeLib())
+    dev = torch.device("meta")
+    q = torch.empty((1, 300, 2, 128), dtype=torch.bfloat16, device=dev)
+    monkeypatch.setattr(mod, "_check_bshd", lambda name, t, dtype: None)
+    monkeypatch.setattr(mod, "_stream_handle", lambda s: None)
+    short = torch.empty((1, 299, 2, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="shape"):
+        mod.attn_fwd_bf16(q, q, q, 0.088, out=short)
+    wrong_dtype = torch.empty((1, 300, 2, 128), dtype=torch.float16, device=dev)
+    with pytest.raises(ValueError, match="bfloat16"):
+        mod.attn_fwd_bf16(q, q, q, 0.088, out=wrong_dtype)
+    good = [torch.empty(shape, dtype=dt, device=dev) for _, shape, dt in mod._prepared_specs(1, 300, 2, 128)]
+    for i in range(6):
+        bad = list(good)
+        bad[i] = torch.empty((1,), dtype=good[i].dtype, device=dev)
+        with pytest.raises(ValueError):
+            mod.sage_prepare(q, q, q, 0.088, out=tuple(bad))
+        with pytest.raises(ValueError):
+            mod.sage_attn_fwd(tuple(bad), 300, 2, 0.088)
+    with pytest.raises(ValueError):
+        mod.sage_prepare(q, q, q, 0.088, out=tuple(good[:5]))
+    assert calls == []  # nothing reached the library
