@@ -15,7 +15,10 @@ Citations (page title, section):
   * quantizer: "gfx1201_sage_prepare / gfx1201_sage_attention" (aiter PR 6390),
     section "Technical Details" (INT8 Q/K with one FP32 scale per 32-row block,
     Q carrying softmax_scale * log2(e); FP8 e4m3 V with one scale per channel,
-    transposed to [B, H, 128, S_pad]).
+    transposed to [B, H, 128, S_pad]);
+  * Q/K row transform: the same page, first commit and "Technical Details"
+    (optional RMSNorm and rotate-half RoPE, rope_dim 32/64/96/128, rounded like
+    the eager PyTorch BF16 sequence).
 """
 import ctypes
 import math
@@ -55,8 +58,11 @@ def _lib():
         lib.oracle_sage_padded_len.restype = ci
         lib.oracle_quant_qk.argtypes = [u16p, ci, ci, ci, ci, cf, ci, i8p, f32p]
         lib.oracle_quant_v.argtypes = [u16p, ci, ci, ci, ci, ci, u8p, f32p]
+        lib.oracle_f32_to_bf16.argtypes = [cf]
+        lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_qk_norm_rope.argtypes = [u16p, ci, ci, ci, ci, u16p, cf, u16p, u16p, ci, u16p]
         for name in ("oracle_softmax_row", "oracle_attn_rows", "oracle_attn_blocked",
-                     "oracle_quant_qk", "oracle_quant_v"):
+                     "oracle_quant_qk", "oracle_quant_v", "oracle_qk_norm_rope"):
             getattr(lib, name).restype = ci
         _LIB = lib
     return _LIB
@@ -184,3 +190,41 @@ def sage_prepare(q, k, v, scale):
     kc, ks = quant_qk(k, 1.0)
     vc, vs = quant_v(v)
     return qc, qs, kc, ks, vc, vs
+
+
+def f32_to_bf16(x):
+    """BF16 bits of fp32 x, round to nearest even (scalar)."""
+    return int(_lib().oracle_f32_to_bf16(float(np.float32(x))))
+
+
+def qk_norm_rope(x, norm_w=None, eps=1e-6, cos=None, sin=None, rope_dim=0):
+    """RoPE(RMSNorm(x)) per (b, s, h) row with BF16 rounding after every step.
+
+    x: BF16 [B, S, H, D]; norm_w: BF16 [D] or None; cos, sin: BF16
+    [>= S, rope_dim] or None.  Returns the BF16 bits, uint16 [B, S, H, D].
+    """
+    x = _bits(x)
+    B, S, H, D = x.shape
+    null = ctypes.POINTER(ctypes.c_uint16)()
+    w = _bits(norm_w) if norm_w is not None else None
+    c = _bits(cos) if rope_dim else None
+    s_ = _bits(sin) if rope_dim else None
+    if rope_dim and (c.shape[-1] != rope_dim or s_.shape[-1] != rope_dim or c.shape[0] < S):
+        raise ValueError("rope tables must be [>= S, rope_dim]")
+    out = np.empty_like(x)
+    _check(_lib().oracle_qk_norm_rope(
+        _ptr(x, ctypes.c_uint16), B, S, H, D,
+        _ptr(w, ctypes.c_uint16) if w is not None else null, float(eps),
+        _ptr(c, ctypes.c_uint16) if rope_dim else null,
+        _ptr(s_, ctypes.c_uint16) if rope_dim else null, int(rope_dim),
+        _ptr(out, ctypes.c_uint16)), "oracle_qk_norm_rope")
+    return out
+
+
+def sage_prepare_fused(q, k, v, scale, q_norm_w=None, k_norm_w=None, eps=1e-6, cos=None,
+                       sin=None, rope_dim=0):
+    """Prepare with the optional Q/K transform: by definition the quantizer
+    applied to qk_norm_rope(q) and qk_norm_rope(k)."""
+    qt = qk_norm_rope(q, q_norm_w, eps, cos, sin, rope_dim)
+    kt = qk_norm_rope(k, k_norm_w, eps, cos, sin, rope_dim)
+    return sage_prepare(qt, kt, v, scale)

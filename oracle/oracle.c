@@ -38,6 +38,27 @@
  *         V codes [B, H, 128, S_pad], V scales [B, H, 128].  Pad rows, pad
  *         columns and pad blocks are 0.
  *
+ *  3. The optional Q/K row transform of the prepare stage (same page, first
+ *     commit and "Technical Details": RMSNorm and rotate-half RoPE with
+ *     rope_dim 32/64/96/128, rounded like the eager PyTorch BF16 sequence).
+ *     Readings (the page names the rounding rule, not the formulas):
+ *       - RMSNorm normalizes each (b, s, h) row over its D channels, as the
+ *         per-head QK norm of a DiT does:
+ *           ms = (sum of fp32(x)^2 over the row) / D           (fp32)
+ *           r  = 1 / sqrt(ms + eps)     (correctly rounded sqrt, then division)
+ *           n  = bf16(fp32(x) * r);     y = bf16(fp32(n) * fp32(w))
+ *         The sum of squares is taken as a pairwise tree over the channels in
+ *         index order ((x0^2 + x1^2) + (x2^2 + x3^2)) + ...; eager PyTorch
+ *         leaves its reduction order unspecified.
+ *       - RoPE rotates the first rope_dim channels with BF16 tables
+ *         cos, sin [S_tab, rope_dim] indexed by the row's token position:
+ *           out[c] = bf16( bf16(y[c] * cos[c]) + bf16(rot[c] * sin[c]) ),
+ *           rot[c] = -y[c + rope_dim/2] (c < rope_dim/2), y[c - rope_dim/2] (else);
+ *         channels c >= rope_dim pass through.  Each BF16 product or sum is
+ *         an fp32 operation rounded to BF16 (round to nearest even), which is
+ *         how eager PyTorch evaluates BF16 tensor arithmetic.
+ *       - RMSNorm (when enabled) comes first, then RoPE, then the quantizer.
+ *
  * Inputs are BF16 bit patterns (uint16) in [B, S, H, D] order.  Build with
  * plain gcc, -O2 -ffp-contract=off, no fast-math: the quantizer must round
  * every fp32 operation exactly as IEEE 754 says.
@@ -376,4 +397,66 @@ int oracle_quant_v(const uint16_t* v, int B, int S, int H, int D, int S_pad, uin
         }
       }
   return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 3. Q/K row transform: RMSNorm and rotate-half RoPE (BF16 rounding)        */
+/* ------------------------------------------------------------------------ */
+
+/* fp32 -> BF16, round to nearest, ties to even (inputs are finite). */
+uint16_t oracle_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  const uint32_t lsb = (u >> 16) & 1u;
+  return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+static float bf16r(float f) { return bf16_to_f32(oracle_f32_to_bf16(f)); }
+
+/* Sum of v[0..n) as a pairwise tree in index order (n a power of two). */
+static float pairwise_sum(const float* v, int n) {
+  if (n == 1) return v[0];
+  return pairwise_sum(v, n / 2) + pairwise_sum(v + n / 2, n / 2);
+}
+
+/*
+ * out = RoPE(RMSNorm(x)) per row, both optional (see the readings at the top).
+ *   x, out   : BF16 [B, S, H, D] (may not alias)
+ *   norm_w   : BF16 [D] or NULL (no RMSNorm); eps its epsilon
+ *   cos_t, sin_t : BF16 [>= S, rope_dim] or NULL when rope_dim == 0
+ *   rope_dim : 0 (no RoPE) or an even number <= D
+ * D must be a power of two <= 128.
+ */
+int oracle_qk_norm_rope(const uint16_t* x, int B, int S, int H, int D, const uint16_t* norm_w,
+                        float eps, const uint16_t* cos_t, const uint16_t* sin_t, int rope_dim,
+                        uint16_t* out) {
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || D > 128 || (D & (D - 1)) != 0) return ORACLE_EINVAL;
+  if (rope_dim < 0 || rope_dim > D || (rope_dim & 1) || (rope_dim && (!cos_t || !sin_t)))
+    return ORACLE_EINVAL;
+  const int half = rope_dim / 2;
+#pragma omp parallel for collapse(3) schedule(static)
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < S; ++i)
+      for (int h = 0; h < H; ++h) {
+        float y[128], sq[128];
+        for (int d = 0; d < D; ++d) y[d] = bf16_to_f32(x[idx_bshd(b, i, h, d, S, H, D)]);
+        if (norm_w) {
+          for (int d = 0; d < D; ++d) sq[d] = y[d] * y[d];
+          const float ms = pairwise_sum(sq, D) / (float)D;
+          const float r = 1.0f / sqrtf(ms + eps);
+          for (int d = 0; d < D; ++d) y[d] = bf16r(bf16r(y[d] * r) * bf16_to_f32(norm_w[d]));
+        }
+        if (rope_dim) {
+          float z[128];
+          for (int c = 0; c < rope_dim; ++c) {
+            const float cs = bf16_to_f32(cos_t[(int64_t)i * rope_dim + c]);
+            const float sn = bf16_to_f32(sin_t[(int64_t)i * rope_dim + c]);
+            const float rot = (c < half) ? -y[c + half] : y[c - half];
+            z[c] = bf16r(bf16r(y[c] * cs) + bf16r(rot * sn));
+          }
+          for (int c = 0; c < rope_dim; ++c) y[c] = z[c];
+        }
+        for (int d = 0; d < D; ++d) out[idx_bshd(b, i, h, d, S, H, D)] = oracle_f32_to_bf16(y[d]);
+      }
+  return ORACLE_OK;
 }

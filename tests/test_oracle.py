@@ -321,3 +321,136 @@ def test_cost_model_reproduces_printed_table():
     assert round(byts / 2 ** 20) == fr["traffic_mib"]
     assert round(flops / byts) == fr["intensity"]
     assert round(max(flops / fr["peak_flops"], byts / fr["bandwidth"]) * 1e6) == fr["time_us"]
+
+
+# --------------------------------------------------------------------------
+# Q/K row transform: RMSNorm + rotate-half RoPE, BF16 rounding
+# ("gfx1201_sage_prepare / gfx1201_sage_attention", first commit and
+# "Technical Details": rounded like the eager PyTorch BF16 sequence)
+# --------------------------------------------------------------------------
+
+def torch_eager_norm_rope(x, w, eps, cos, sin, rope_dim):
+    """The eager PyTorch BF16 sequence, op by op (each op rounds to BF16)."""
+    y = x
+    if w is not None:
+        xf = y.float()
+        y = (xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps)).to(torch.bfloat16) * w
+    if rope_dim:
+        S = x.shape[1]
+        half = rope_dim // 2
+        yr, yp = y[..., :rope_dim], y[..., rope_dim:]
+        rot = torch.cat((-yr[..., half:], yr[..., :half]), dim=-1)
+        c = cos[:S].view(1, S, 1, rope_dim)
+        s = sin[:S].view(1, S, 1, rope_dim)
+        y = torch.cat((yr * c + rot * s, yp), dim=-1)
+    return y
+
+
+def rope_tables(S, rope_dim, base=10000.0):
+    """BF16 cos/sin tables [S, rope_dim] of the rotate-half form (halves repeat)."""
+    half = rope_dim // 2
+    inv = 1.0 / base ** (torch.arange(half, dtype=torch.float64) / half)
+    ang = torch.arange(S, dtype=torch.float64)[:, None] * inv[None, :]
+    ang = torch.cat((ang, ang), dim=-1)
+    return torch.cos(ang).to(torch.bfloat16), torch.sin(ang).to(torch.bfloat16)
+
+
+def as_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+
+def test_f32_to_bf16_rounds_to_nearest_even():
+    g = torch.Generator().manual_seed(11)
+    vals = torch.randn(3000, generator=g) * torch.exp2(torch.randint(-40, 40, (3000,), generator=g).float())
+    # exact midpoints between BF16 neighbours, with even and odd upper halves
+    hi = torch.randint(0x0080, 0x7F00, (2000,), generator=g, dtype=torch.int32)
+    mids = ((hi << 16) | 0x8000).view(torch.float32)
+    for x in torch.cat((vals, mids, -mids)).tolist():
+        ref = int(torch.tensor([x], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).item()) & 0xFFFF
+        assert oracle.f32_to_bf16(x) == ref, x
+
+
+@pytest.mark.parametrize("rope_dim", [0, 32, 64, 96, 128])
+@pytest.mark.parametrize("norm", [False, True])
+def test_norm_rope_equals_torch_eager_on_exact_sums(rope_dim, norm):
+    # inputs k/16 with |k| < 128: every square is a multiple of 2^-8 below 64, so
+    # the fp32 sum of squares is exact in any order and torch must agree bitwise
+    B, S, H, D = 2, 40, 3, 128
+    g = torch.Generator().manual_seed(100 + rope_dim + norm)
+    x = (torch.randint(-127, 128, (B, S, H, D), generator=g).float() / 16).to(torch.bfloat16)
+    w = (1 + 0.25 * torch.randn(D, generator=g)).to(torch.bfloat16) if norm else None
+    cos, sin = rope_tables(S + 5, rope_dim) if rope_dim else (None, None)
+    ref = torch_eager_norm_rope(x, w, 1e-6, cos, sin, rope_dim)
+    got = as_bf16(oracle.qk_norm_rope(x, w, 1e-6, cos, sin, rope_dim))
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("rope_dim", [32, 96, 128])
+def test_norm_rope_close_to_torch_eager_on_randn(rope_dim):
+    # random rows: only the (unspecified) order of torch's fp32 sum of squares can
+    # differ, which moves a BF16 result by at most one unit in the last place
+    B, S, H, D = 1, 64, 4, 128
+    g = torch.Generator().manual_seed(7 + rope_dim)
+    x = (3 * torch.randn((B, S, H, D), generator=g)).to(torch.bfloat16)
+    w = (1 + 0.25 * torch.randn(D, generator=g)).to(torch.bfloat16)
+    cos, sin = rope_tables(S, rope_dim)
+    ref = torch_eager_norm_rope(x, w, 1e-6, cos, sin, rope_dim)
+    got = as_bf16(oracle.qk_norm_rope(x, w, 1e-6, cos, sin, rope_dim))
+    same = (got.view(torch.int16) == ref.view(torch.int16)).float().mean().item()
+    assert same >= 0.99, same
+    ulp = torch.abs(got.float() - ref.float()) / torch.exp2(torch.floor(torch.log2(ref.float().abs().clamp_min(1e-30))) - 7)
+    assert ulp.max().item() <= 2.0
+
+
+def test_rmsnorm_closed_forms():
+    D = 128
+    # constant row a: mean square a^2, so x * rsqrt(a^2) = sign(a) exactly (eps = 0)
+    for a in (0.5, -3.0, 1.0, 96.0):
+        x = torch.full((1, 1, 1, D), a).to(torch.bfloat16)
+        got = as_bf16(oracle.qk_norm_rope(x, torch.ones(D, dtype=torch.bfloat16), 0.0))
+        assert torch.equal(got.float(), torch.full((1, 1, 1, D), math.copysign(1.0, a)))
+    # one nonzero channel a: x * r = sign(a) * sqrt(128), rounded to BF16 = 11.3125
+    x = torch.zeros((1, 1, 1, D))
+    x[..., 5] = 4.0
+    got = as_bf16(oracle.qk_norm_rope(x.to(torch.bfloat16), torch.ones(D, dtype=torch.bfloat16), 0.0)).float()
+    assert got[0, 0, 0, 5].item() == 11.3125 and float(got.abs().sum()) == 11.3125
+    # the weight multiplies channel by channel
+    w = torch.arange(1, D + 1, dtype=torch.float32).to(torch.bfloat16)
+    x = torch.full((1, 1, 1, D), 2.0).to(torch.bfloat16)
+    got = as_bf16(oracle.qk_norm_rope(x, w, 0.0)).float()
+    assert torch.equal(got.flatten(), w.float())
+
+
+@pytest.mark.parametrize("rope_dim", [32, 64, 96, 128])
+def test_rope_special_tables(rope_dim):
+    B, S, H, D = 1, 9, 2, 128
+    g = torch.Generator().manual_seed(rope_dim)
+    x = torch.randn((B, S, H, D), generator=g).to(torch.bfloat16)
+    one = torch.ones((S, rope_dim), dtype=torch.bfloat16)
+    zero = torch.zeros((S, rope_dim), dtype=torch.bfloat16)
+    # angle 0: identity
+    assert torch.equal(as_bf16(oracle.qk_norm_rope(x, None, 0.0, one, zero, rope_dim)), x)
+    # angle pi/2: exactly rotate_half on the rotated channels, the rest untouched
+    got = as_bf16(oracle.qk_norm_rope(x, None, 0.0, zero, one, rope_dim))
+    half = rope_dim // 2
+    exp = x.clone()
+    exp[..., :half] = -x[..., half:rope_dim]
+    exp[..., half:rope_dim] = x[..., :half]
+    assert torch.equal(got, exp)
+
+
+def test_rope_matches_the_rotation_in_fp64():
+    # pins the pairing of channel c with c + rope_dim/2, the sign of the rotated
+    # half and the position index of the table row
+    B, S, H, D, rd = 1, 50, 2, 128, 64
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn((B, S, H, D), generator=g).to(torch.bfloat16)
+    cos, sin = rope_tables(S, rd)
+    got = as_bf16(oracle.qk_norm_rope(x, None, 0.0, cos, sin, rd)).double()
+    xd, cd, sd = x.double(), cos.double()[None, :, None, :], sin.double()[None, :, None, :]
+    half = rd // 2
+    x1, x2 = xd[..., :half], xd[..., half:rd]
+    exp = torch.cat((x1 * cd[..., :half] - x2 * sd[..., :half], x2 * cd[..., half:] + x1 * sd[..., half:]), -1)
+    err = (got[..., :rd] - exp).abs().max().item()
+    assert err <= 3 * 2.0 ** -8 * xd.abs().max().item(), err
+    assert torch.equal(got[..., rd:], xd[..., rd:])
