@@ -17,8 +17,9 @@ kernel on it, with no staging copies and no second GPU context.
 import ctypes
 import os
 
-__all__ = ["DitAttnError", "load", "abi_version", "sage_padded_len", "attn_fwd_bf16",
-           "sage_prepare", "sage_attn_fwd", "sage_attention", "HEAD_DIM", "LIB_PATH"]
+__all__ = ["DitAttnError", "load", "abi_version", "sage_padded_len", "sage_workspace_size",
+           "attn_fwd_bf16", "sage_prepare", "sage_prepare_ex", "qk_norm_rope_bf16", "sage_attn_fwd",
+           "sage_attention", "HEAD_DIM", "LIB_PATH"]
 
 HEAD_DIM = 128
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
@@ -51,7 +52,13 @@ def load(path=None):
     lib.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, vp]
     lib.sage_prepare.argtypes = [vp] * 9 + [ci, ci, ci, ci, cf, vp]
     lib.sage_attn_fwd.argtypes = [vp] * 7 + [ci, ci, ci, ci, cf, vp]
-    for name in ("attn_fwd_bf16", "sage_prepare", "sage_attn_fwd"):
+    lib.sage_prepare_ex.argtypes = ([vp] * 9 + [ci] * 6 + [cf, vp, vp, cf, vp, vp, ci, vp, vp,
+                                                          ctypes.c_size_t, vp])
+    lib.qk_norm_rope_bf16.argtypes = [vp, vp, ci, ci, ci, ci, vp, cf, vp, vp, ci, vp]
+    lib.ditattn_sage_workspace_size.argtypes = [ci, ci, ci]
+    lib.ditattn_sage_workspace_size.restype = ctypes.c_size_t
+    for name in ("attn_fwd_bf16", "sage_prepare", "sage_attn_fwd", "sage_prepare_ex",
+                 "qk_norm_rope_bf16"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -71,6 +78,11 @@ def sage_padded_len(S):
     if n < 0:
         raise ValueError("invalid sequence length %r" % (S,))
     return n
+
+
+def sage_workspace_size(B, S_kv, H_kv):
+    """Bytes of workspace sage_prepare_ex needs for K smoothing."""
+    return int(load().ditattn_sage_workspace_size(int(B), int(S_kv), int(H_kv)))
 
 
 def _stream_handle(stream):
@@ -119,13 +131,16 @@ def _check_out(name, t, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
-def _prepared_specs(B, S, H, D):
-    """(name, shape, dtype) of the six tensors sage_prepare writes."""
+def _prepared_specs(B, S, H, D, S_kv=None, H_kv=None):
+    """(name, shape, dtype) of the six tensors sage_prepare writes (Q side with S, H;
+    K and V sides with S_kv, H_kv, by default the same)."""
     import torch
-    Sp = sage_padded_len(S)
-    return (("q_i8", (B, H, Sp, D), torch.int8), ("q_scale", (B, H, Sp // 32), torch.float32),
-            ("k_i8", (B, H, Sp, D), torch.int8), ("k_scale", (B, H, Sp // 32), torch.float32),
-            ("v_fp8", (B, H, D, Sp), torch.uint8), ("v_scale", (B, H, D), torch.float32))
+    S_kv = S if S_kv is None else S_kv
+    H_kv = H if H_kv is None else H_kv
+    Sq, Sk = sage_padded_len(S), sage_padded_len(S_kv)
+    return (("q_i8", (B, H, Sq, D), torch.int8), ("q_scale", (B, H, Sq // 32), torch.float32),
+            ("k_i8", (B, H_kv, Sk, D), torch.int8), ("k_scale", (B, H_kv, Sk // 32), torch.float32),
+            ("v_fp8", (B, H_kv, D, Sk), torch.uint8), ("v_scale", (B, H_kv, D), torch.float32))
 
 
 def _dims(q):
@@ -180,6 +195,102 @@ def sage_prepare(q, k, v, scale, out=None, stream=None):
     st = lib.sage_prepare(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S, H, D,
                           float(scale), _stream_handle(stream))
     _status(lib, "sage_prepare", st)
+    return out
+
+
+def _opt_ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check_small(name, t, shape, dtype, device):
+    if t is not None:
+        _check_out(name, t, shape, dtype, device)
+
+
+def sage_prepare_ex(q, k, v, scale, q_norm_w=None, k_norm_w=None, norm_eps=1e-6, rope_cos=None,
+                    rope_sin=None, rope_dim=0, smooth_k=False, out=None, k_mean=None,
+                    workspace=None, stream=None):
+    """sage_prepare with the optional Q/K transform (RMSNorm weights [128] BF16,
+    RoPE tables [>= max(S_q, S_kv), rope_dim] BF16), K smoothing and
+    cross-attention / grouped-query shapes: q [B, S_q, H, 128], k and v
+    [B, S_kv, H_kv, 128].  Returns the six prepared tensors, plus the K channel
+    mean [B, H_kv, 128] fp32 when smooth_k."""
+    import torch
+    lib = load()
+    B, S_q, H, D = _dims(q)
+    _, S_kv, H_kv, _ = _dims(k)
+    _check_bshd("q", q, torch.bfloat16)
+    for name, t in (("k", k), ("v", v)):
+        _check_bshd(name, t, torch.bfloat16)
+        if tuple(t.shape) != (B, S_kv, H_kv, D):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S_kv, H_kv, D)))
+    dev = q.device
+    _check_small("q_norm_w", q_norm_w, (D,), torch.bfloat16, dev)
+    _check_small("k_norm_w", k_norm_w, (D,), torch.bfloat16, dev)
+    if rope_dim:
+        n_tab = max(S_q, S_kv)
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            if t is None or t.dim() != 2 or t.shape[0] < n_tab or t.shape[1] != rope_dim:
+                raise ValueError("%s must be [>= %d, %d]" % (name, n_tab, rope_dim))
+            _check_out(name, t, tuple(t.shape), torch.bfloat16, dev)
+    specs = _prepared_specs(B, S_q, H, D, S_kv, H_kv)
+    if out is None:
+        out = tuple(torch.empty(shape, dtype=dt, device=dev) for _, shape, dt in specs)
+        _on_stream(out, stream)
+    else:
+        if len(out) != 6:
+            raise ValueError("out must be the 6 tensors of a sage_prepare result")
+        for t, (name, shape, dt) in zip(out, specs):
+            _check_out(name, t, shape, dt, dev)
+    ws_bytes = 0
+    if smooth_k:
+        if k_mean is None:
+            k_mean = torch.empty((B, H_kv, D), dtype=torch.float32, device=dev)
+            _on_stream([k_mean], stream)
+        _check_out("k_mean", k_mean, (B, H_kv, D), torch.float32, dev)
+        ws_bytes = sage_workspace_size(B, S_kv, H_kv)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+            _on_stream([workspace], stream)
+        elif workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous buffer of >= %d bytes" % ws_bytes)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        k_mean = workspace = None
+    st = lib.sage_prepare_ex(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S_q, S_kv, H,
+                             H_kv, D, float(scale), _opt_ptr(q_norm_w), _opt_ptr(k_norm_w),
+                             float(norm_eps), _opt_ptr(rope_cos if rope_dim else None),
+                             _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
+                             _opt_ptr(k_mean), _opt_ptr(workspace), ws_bytes, _stream_handle(stream))
+    _status(lib, "sage_prepare_ex", st)
+    return tuple(out) + ((k_mean,) if smooth_k else ())
+
+
+def qk_norm_rope_bf16(x, norm_w=None, norm_eps=1e-6, rope_cos=None, rope_sin=None, rope_dim=0,
+                      out=None, stream=None):
+    """The Q/K row transform of sage_prepare_ex alone: BF16 [B, S, H, 128] in and out
+    (out may be x itself)."""
+    import torch
+    lib = load()
+    B, S, H, D = _dims(x)
+    _check_bshd("x", x, torch.bfloat16)
+    dev = x.device
+    _check_small("norm_w", norm_w, (D,), torch.bfloat16, dev)
+    if rope_dim:
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            if t is None or t.dim() != 2 or t.shape[0] < S or t.shape[1] != rope_dim:
+                raise ValueError("%s must be [>= %d, %d]" % (name, S, rope_dim))
+            _check_out(name, t, tuple(t.shape), torch.bfloat16, dev)
+    if out is None:
+        out = torch.empty_like(x)
+        _on_stream([out], stream)
+    else:
+        _check_out("out", out, (B, S, H, D), torch.bfloat16, dev)
+    st = lib.qk_norm_rope_bf16(_ptr(x), _ptr(out), B, S, H, D, _opt_ptr(norm_w), float(norm_eps),
+                               _opt_ptr(rope_cos if rope_dim else None),
+                               _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
+                               _stream_handle(stream))
+    _status(lib, "qk_norm_rope_bf16", st)
     return out
 
 

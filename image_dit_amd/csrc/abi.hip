@@ -15,27 +15,52 @@ constexpr double kLog2eD = 1.4426950408889634;
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return a0 < b0 + static_cast<uintptr_t>(nb) && b0 < a0 + static_cast<uintptr_t>(na);
 }
 
-// Shared shape checks.  On success *elems = B * S * H * 128 and *s_pad = S_pad.
+int64_t padded(int S) { return (static_cast<int64_t>(S) + 255) / 256 * 256; }
+
+// Sizes of one attention problem: queries [B, S_q, H, D], keys/values [B, S_kv, H_kv, D].
 // The bounds are the ranges the kernels index in:
-//   * B * H * S_pad <= INT32_MAX: tile, block and grid indices are int, and
-//     every grid times its workgroup size stays below 2^32 work-items;
+//   * B * H * S_pad <= INT32_MAX on either side: tile, block and grid indices are
+//     int, and every grid times its workgroup size stays below 2^32 work-items;
 //   * H <= DITATTN_MAX_HEADS: the BF16 kernel addresses a K/V tile row as a
-//     32-bit byte offset r * H * 256 with r < 64 (63 * 65536 * 256 < 2^32).
-int check_shape(int B, int S, int H, int D, float scale, int64_t* elems, int* s_pad) {
-  if (B < 1 || S < 1 || H < 1) return DITATTN_EINVAL;
+//     32-bit byte offset r * H_kv * 256 with r < 64 (63 * 65536 * 256 < 2^32).
+int check_sizes(int B, int S_q, int S_kv, int H, int H_kv, int D, float scale) {
+  if (B < 1 || S_q < 1 || S_kv < 1 || H < 1 || H_kv < 1) return DITATTN_EINVAL;
   if (!isfinite(scale) || !(scale > 0.0f)) return DITATTN_EINVAL;
+  if (H % H_kv != 0) return DITATTN_EINVAL;
   if (D != 128) return DITATTN_EUNSUPPORTED;
   if (H > DITATTN_MAX_HEADS) return DITATTN_EOVERFLOW;
-  if (S > (INT32_MAX - 255)) return DITATTN_EOVERFLOW;
-  const int64_t sp = (static_cast<int64_t>(S) + 255) / 256 * 256;
-  const int64_t bh = static_cast<int64_t>(B) * H;  // < 2^31 * 2^16: no int64 overflow
-  if (bh * sp > INT32_MAX) return DITATTN_EOVERFLOW;
-  *elems = bh * S * 128;
-  *s_pad = static_cast<int>(sp);
+  if (S_q > INT32_MAX - 255 || S_kv > INT32_MAX - 255) return DITATTN_EOVERFLOW;
+  if (static_cast<int64_t>(B) * H * padded(S_q) > INT32_MAX) return DITATTN_EOVERFLOW;
+  if (static_cast<int64_t>(B) * H_kv * padded(S_kv) > INT32_MAX) return DITATTN_EOVERFLOW;
+  return DITATTN_OK;
+}
+
+int check_shape(int entry, int B, int S, int H, int D, float scale) {
+  const int st = check_sizes(B, S, S, H, H, D, scale);
+  if (st != DITATTN_OK) return st;
+  switch (entry) {
+    case DITATTN_ENTRY_ATTN_FWD_BF16:
+    case DITATTN_ENTRY_SAGE_PREPARE: return DITATTN_OK;
+    // the Sage kernel addresses a V^T tile row as a 32-bit byte offset c * S_pad, c < 128
+    case DITATTN_ENTRY_SAGE_ATTN_FWD: return S > DITATTN_MAX_SEQ_SAGE ? DITATTN_EOVERFLOW : DITATTN_OK;
+    default: return DITATTN_EINVAL;
+  }
+}
+
+// The optional Q/K row transform (RMSNorm weights, RoPE tables).
+int check_xform(const void* norm_w0, const void* norm_w1, float eps, const void* cos_t,
+                const void* sin_t, int rope_dim) {
+  if (!isfinite(eps) || eps < 0.0f) return DITATTN_EINVAL;
+  if (rope_dim != 0 && rope_dim != 32 && rope_dim != 64 && rope_dim != 96 && rope_dim != 128)
+    return DITATTN_EUNSUPPORTED;
+  if (rope_dim && (!cos_t || !sin_t)) return DITATTN_EINVAL;
+  if (misaligned(norm_w0) || misaligned(norm_w1)) return DITATTN_EALIGN;
+  if (rope_dim && (misaligned(cos_t) || misaligned(sin_t))) return DITATTN_EALIGN;
   return DITATTN_OK;
 }
 
@@ -50,8 +75,10 @@ int ditattn_abi_version(void) { return DITATTN_ABI_VERSION; }
 const char* ditattn_status_string(int status) {
   switch (status) {
     case DITATTN_OK: return "ok";
-    case DITATTN_EINVAL: return "invalid argument (size < 1, null pointer, bad scale or aliased output)";
-    case DITATTN_EUNSUPPORTED: return "unsupported head dim (only D = 128)";
+    case DITATTN_EINVAL:
+      return "invalid argument (size < 1, null pointer, bad scale or eps, H not a multiple of H_kv, "
+             "short workspace or aliased output)";
+    case DITATTN_EUNSUPPORTED: return "unsupported head dim (only D = 128) or rope_dim (0, 32, 64, 96, 128)";
     case DITATTN_EALIGN: return "pointer not 16-byte aligned";
     case DITATTN_EOVERFLOW: return "size exceeds what the kernels index";
     case DITATTN_EHIP: return "HIP launch failed";
@@ -65,27 +92,21 @@ int ditattn_sage_padded_len(int S) {
 }
 
 int ditattn_check_shape(int entry, int B, int S, int H, int D, float scale) {
-  int64_t elems;
-  int s_pad;
-  int st = check_shape(B, S, H, D, scale, &elems, &s_pad);
-  if (st != DITATTN_OK) return st;
-  switch (entry) {
-    case DITATTN_ENTRY_ATTN_FWD_BF16:
-    case DITATTN_ENTRY_SAGE_PREPARE: return DITATTN_OK;
-    case DITATTN_ENTRY_SAGE_ATTN_FWD: return S > DITATTN_MAX_SEQ_SAGE ? DITATTN_EOVERFLOW : DITATTN_OK;
-    default: return DITATTN_EINVAL;
-  }
+  return check_shape(entry, B, S, H, D, scale);
+}
+
+size_t ditattn_sage_workspace_size(int B, int S_kv, int H_kv) {
+  if (check_sizes(B, S_kv, S_kv, H_kv, H_kv, 128, 1.0f) != DITATTN_OK) return 0;
+  return ditattn::sage_workspace_bytes(B, S_kv, H_kv);
 }
 
 int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, int S, int H,
                   int D, float scale, hipStream_t stream) {
-  int64_t elems;
-  int s_pad;
-  int st = check_shape(B, S, H, D, scale, &elems, &s_pad);
+  int st = check_shape(DITATTN_ENTRY_ATTN_FWD_BF16, B, S, H, D, scale);
   if (st != DITATTN_OK) return st;
   if (!q || !k || !v || !o) return DITATTN_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return DITATTN_EALIGN;
-  const int64_t bytes = elems * 2;
+  const int64_t bytes = static_cast<int64_t>(B) * S * H * 256;
   if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
     return DITATTN_EINVAL;
   if (ditattn::launch_attn_fwd_bf16(q, k, v, o, B, S, H, log2e_scale(scale), stream) != hipSuccess)
@@ -93,34 +114,78 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, i
   return DITATTN_OK;
 }
 
-int sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8, float* q_scale,
-                 int8_t* k_i8, float* k_scale, uint8_t* v_fp8, float* v_scale, int B, int S,
-                 int H, int D, float scale, hipStream_t stream) {
-  int64_t elems;
-  int s_pad;
-  int st = check_shape(B, S, H, D, scale, &elems, &s_pad);
+int sage_prepare_ex(const void* q, const void* k, const void* v, int8_t* q_i8, float* q_scale,
+                    int8_t* k_i8, float* k_scale, uint8_t* v_fp8, float* v_scale, int B, int S_q,
+                    int S_kv, int H, int H_kv, int D, float scale, const void* q_norm_w,
+                    const void* k_norm_w, float norm_eps, const void* rope_cos,
+                    const void* rope_sin, int rope_dim, float* k_mean, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  int st = check_sizes(B, S_q, S_kv, H, H_kv, D, scale);
+  if (st != DITATTN_OK) return st;
+  st = check_xform(q_norm_w, k_norm_w, norm_eps, rope_cos, rope_sin, rope_dim);
   if (st != DITATTN_OK) return st;
   const void* ptrs[9] = {q, k, v, q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale};
   for (const void* p : ptrs)
     if (!p) return DITATTN_EINVAL;
+  if (k_mean && !workspace) return DITATTN_EINVAL;
   for (const void* p : ptrs)
     if (misaligned(p)) return DITATTN_EALIGN;
-  const int64_t bh = static_cast<int64_t>(B) * H;
-  const int64_t in_bytes = elems * 2;
-  const int64_t code_bytes = bh * s_pad * 128;
-  const int64_t qk_scale_bytes = bh * (s_pad / 32) * 4;
-  const int64_t v_scale_bytes = bh * 128 * 4;
-  const void* outs[6] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale};
-  const int64_t out_bytes[6] = {code_bytes, qk_scale_bytes, code_bytes, qk_scale_bytes, code_bytes, v_scale_bytes};
-  const void* ins[3] = {q, k, v};
-  for (int a = 0; a < 6; ++a) {
-    for (int i = 0; i < 3; ++i)
-      if (overlaps(outs[a], out_bytes[a], ins[i], in_bytes)) return DITATTN_EINVAL;
-    for (int b2 = a + 1; b2 < 6; ++b2)
+  if (misaligned(k_mean) || misaligned(workspace)) return DITATTN_EALIGN;
+  const size_t ws_need = k_mean ? ditattn::sage_workspace_bytes(B, S_kv, H_kv) : 0;
+  if (k_mean && workspace_bytes < ws_need) return DITATTN_EINVAL;
+  const int64_t sqp = padded(S_q), skp = padded(S_kv);
+  const int64_t bhq = static_cast<int64_t>(B) * H, bhk = static_cast<int64_t>(B) * H_kv;
+  const int64_t q_bytes = bhq * S_q * 256, kv_bytes = bhk * S_kv * 256;
+  void* const outs[8] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, k_mean, workspace};
+  const int64_t out_bytes[8] = {bhq * sqp * 128, bhq * (sqp / 32) * 4, bhk * skp * 128,
+                                bhk * (skp / 32) * 4, bhk * skp * 128, bhk * 128 * 4,
+                                bhk * 128 * 4, static_cast<int64_t>(ws_need)};
+  // the tables have a row per token position up to max(S_q, S_kv); a weight is 256 B
+  const int64_t tab = static_cast<int64_t>(S_q > S_kv ? S_q : S_kv) * rope_dim * 2;
+  const void* ins[7] = {q, k, v, q_norm_w, k_norm_w, rope_dim ? rope_cos : nullptr,
+                        rope_dim ? rope_sin : nullptr};
+  const int64_t in_bytes[7] = {q_bytes, kv_bytes, kv_bytes, 256, 256, tab, tab};
+  for (int a = 0; a < 8; ++a) {
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(outs[a], out_bytes[a], ins[i], in_bytes[i])) return DITATTN_EINVAL;
+    for (int b2 = a + 1; b2 < 8; ++b2)
       if (overlaps(outs[a], out_bytes[a], outs[b2], out_bytes[b2])) return DITATTN_EINVAL;
   }
-  if (ditattn::launch_sage_prepare(q, k, v, q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, B, S, H,
-                                   s_pad, log2e_scale(scale), stream) != hipSuccess)
+  ditattn::PrepareArgs a{q, k, v, q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale,
+                         B, S_q, S_kv, H, H_kv, log2e_scale(scale), q_norm_w, k_norm_w, norm_eps,
+                         rope_dim ? rope_cos : nullptr, rope_dim ? rope_sin : nullptr, rope_dim,
+                         k_mean, workspace};
+  if (ditattn::launch_sage_prepare(a, stream) != hipSuccess) return DITATTN_EHIP;
+  return DITATTN_OK;
+}
+
+int sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8, float* q_scale,
+                 int8_t* k_i8, float* k_scale, uint8_t* v_fp8, float* v_scale, int B, int S,
+                 int H, int D, float scale, hipStream_t stream) {
+  return sage_prepare_ex(q, k, v, q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, B, S, S, H, H, D,
+                         scale, nullptr, nullptr, 0.0f, nullptr, nullptr, 0, nullptr, nullptr, 0,
+                         stream);
+}
+
+int qk_norm_rope_bf16(const void* x, void* out, int B, int S, int H, int D, const void* norm_w,
+                      float norm_eps, const void* rope_cos, const void* rope_sin, int rope_dim,
+                      hipStream_t stream) {
+  int st = check_sizes(B, S, S, H, H, D, 1.0f);
+  if (st != DITATTN_OK) return st;
+  st = check_xform(norm_w, nullptr, norm_eps, rope_cos, rope_sin, rope_dim);
+  if (st != DITATTN_OK) return st;
+  if (!x || !out) return DITATTN_EINVAL;
+  if (misaligned(x) || misaligned(out)) return DITATTN_EALIGN;
+  const int64_t bytes = static_cast<int64_t>(B) * S * H * 256;
+  const int64_t tab = static_cast<int64_t>(S) * rope_dim * 2;
+  // in place (out == x) is allowed: every row fragment is read before the same lane
+  // writes it; any other overlap is not
+  if (out != x && overlaps(out, bytes, x, bytes)) return DITATTN_EINVAL;
+  if (overlaps(out, bytes, norm_w, 256) || (rope_dim && (overlaps(out, bytes, rope_cos, tab) ||
+                                                         overlaps(out, bytes, rope_sin, tab))))
+    return DITATTN_EINVAL;
+  if (ditattn::launch_qk_norm_rope(x, out, B, S, H, norm_w, norm_eps, rope_dim ? rope_cos : nullptr,
+                                   rope_dim ? rope_sin : nullptr, rope_dim, stream) != hipSuccess)
     return DITATTN_EHIP;
   return DITATTN_OK;
 }
@@ -128,27 +193,25 @@ int sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8, floa
 int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                   const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
                   int B, int S, int H, int D, float scale, hipStream_t stream) {
-  int64_t elems;
-  int s_pad;
-  int st = check_shape(B, S, H, D, scale, &elems, &s_pad);
+  int st = check_shape(DITATTN_ENTRY_SAGE_ATTN_FWD, B, S, H, D, scale);
   if (st != DITATTN_OK) return st;
-  // the kernel addresses a V^T tile row as a 32-bit byte offset c * S_pad, c < 128
-  if (S > DITATTN_MAX_SEQ_SAGE) return DITATTN_EOVERFLOW;
   const void* ptrs[7] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o};
   for (const void* p : ptrs)
     if (!p) return DITATTN_EINVAL;
   for (const void* p : ptrs)
     if (misaligned(p)) return DITATTN_EALIGN;
   const int64_t bh = static_cast<int64_t>(B) * H;
+  const int64_t s_pad = padded(S);
   const int64_t code_bytes = bh * s_pad * 128;
   const int64_t qk_scale_bytes = bh * (s_pad / 32) * 4;
   const int64_t v_scale_bytes = bh * 128 * 4;
   const void* ins[6] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale};
-  const int64_t in_bytes[6] = {code_bytes, qk_scale_bytes, code_bytes, qk_scale_bytes, code_bytes, v_scale_bytes};
+  const int64_t in_bytes[6] = {code_bytes, qk_scale_bytes, code_bytes, qk_scale_bytes, code_bytes,
+                               v_scale_bytes};
   for (int i = 0; i < 6; ++i)
-    if (overlaps(o, elems * 2, ins[i], in_bytes[i])) return DITATTN_EINVAL;
+    if (overlaps(o, bh * S * 256, ins[i], in_bytes[i])) return DITATTN_EINVAL;
   if (ditattn::launch_sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S, H,
-                                    s_pad, stream) != hipSuccess)
+                                    static_cast<int>(s_pad), stream) != hipSuccess)
     return DITATTN_EHIP;
   return DITATTN_OK;
 }

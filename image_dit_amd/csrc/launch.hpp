@@ -13,9 +13,32 @@ namespace ditattn {
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B,
                                 int S, int H, float c, hipStream_t stream);
 
-hipError_t launch_sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8,
-                               float* q_scale, int8_t* k_i8, float* k_scale, uint8_t* v_fp8,
-                               float* v_scale, int B, int S, int H, int S_pad, float c,
+// Everything sage_prepare / sage_prepare_ex pass to the prepare kernels.
+struct PrepareArgs {
+  const void *q, *k, *v;  // BF16 [B, S_q, H, 128] and [B, S_kv, H_kv, 128]
+  int8_t* q_i8;
+  float* q_scale;
+  int8_t* k_i8;
+  float* k_scale;
+  uint8_t* v_fp8;
+  float* v_scale;
+  int B, S_q, S_kv, H, H_kv;
+  float c;                             // float(double(scale) * log2(e))
+  const void *q_norm_w, *k_norm_w;     // BF16 [128] or nullptr
+  float eps;
+  const void *rope_cos, *rope_sin;     // BF16 [>= max(S_q, S_kv), rope_dim]
+  int rope_dim;                        // 0 = no RoPE
+  float* k_mean;                       // [B, H_kv, 128]: K smoothing on, or nullptr
+  void* workspace;                     // >= sage_workspace_bytes(B, S_kv, H_kv) when k_mean
+};
+
+hipError_t launch_sage_prepare(const PrepareArgs& a, hipStream_t stream);
+
+// Bytes of workspace the K-smoothing pass needs (fp64 partial channel sums).
+size_t sage_workspace_bytes(int B, int S_kv, int H_kv);
+
+hipError_t launch_qk_norm_rope(const void* x, void* out, int B, int S, int H, const void* norm_w,
+                               float eps, const void* cos_t, const void* sin_t, int rope_dim,
                                hipStream_t stream);
 
 hipError_t launch_sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,

@@ -45,56 +45,140 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// ---------------------------------------------------------------- Q/K row transform
+// Optional RMSNorm and rotate-half RoPE of a Q or K row before it is quantized,
+// rounded like the eager BF16 sequence: n = bf16(x * r) with r = 1 / sqrt(mean(x^2) + eps),
+// y = bf16(n * w); then out = bf16(bf16(y * cos) + bf16(rot(y) * sin)) on the first
+// rope_dim channels, rot(y)[c] = -y[c + rope_dim/2] below rope_dim/2, y[c - rope_dim/2] above.
+// The sum of squares is a pairwise tree over the channels in index order.
+struct RowXform {
+  const uint16_t* norm_w;  // BF16 [128] RMSNorm weight, or nullptr (no RMSNorm)
+  float eps;
+  const uint16_t* cos_t;   // BF16 [S_tab, rope_dim], row = token position
+  const uint16_t* sin_t;
+  int rope_dim;            // 0 (no RoPE), 32, 64, 96 or 128
+};
+
+__device__ __forceinline__ float round_bf16(float x) { return (float)(__bf16)x; }
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& raw, float (&y)[8]) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[2 * e] = bf16_bits_to_f32(w[e] & 0xFFFFu);
+    y[2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
+  }
+}
+
+// y: channels 8 * chunk + 0..7 of one row at token position `tok`; the 16 lanes with
+// the same lane >> 4 hold the 16 fragments of that row.  Every lane of the wave
+// calls this together (it shuffles); rows with valid == false come out as zeros.
+__device__ __forceinline__ void xform_fragment(float (&y)[8], int chunk, int tok, bool valid,
+                                               const RowXform& t) {
+#pragma clang fp contract(off)
+  if (t.norm_w) {
+    float sq[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq[e] = y[e] * y[e];
+    float s = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+#pragma unroll
+    for (int off = 1; off <= 8; off <<= 1) s = s + __shfl_xor(s, off, 64);
+    const float r = 1.0f / sqrtf(s / 128.0f + t.eps);
+    float w[8];
+    unpack_bf16x8(*(const uint4*)(t.norm_w + 8 * chunk), w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = round_bf16(round_bf16(y[e] * r) * w[e]);
+  }
+  if (t.rope_dim) {
+    const int lane = threadIdx.x & 63;
+    const bool rot_lane = 8 * chunk < t.rope_dim;
+    const bool lower = 16 * chunk < t.rope_dim;   // channel < rope_dim / 2
+    const int hc = t.rope_dim >> 4;               // rope_dim / 2 in 8-channel chunks
+    const int src = rot_lane ? (lower ? lane + hc : lane - hc) : lane;
+    float part[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[e] = __shfl(y[e], src, 64);
+    if (rot_lane && valid) {
+      float cs[8], sn[8];
+      const int64_t o = (int64_t)tok * t.rope_dim + 8 * chunk;
+      unpack_bf16x8(*(const uint4*)(t.cos_t + o), cs);
+      unpack_bf16x8(*(const uint4*)(t.sin_t + o), sn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float rot = lower ? -part[e] : part[e];
+        y[e] = round_bf16(round_bf16(y[e] * cs[e]) + round_bf16(rot * sn[e]));
+      }
+    }
+  }
+  if (!valid) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+  }
+}
+
 // ---------------------------------------------------------------- Q and K
-// grid.x: ceil(B * H * nblk / 4) workgroups of 4 waves; grid.y: 0 = Q, 1 = K.
+// One side (Q or K) of the quantizer.
+struct QuantSide {
+  const uint16_t* x;  // BF16 [B, S, H, 128]
+  int8_t* codes;      // [B, H, S_pad, 128]
+  float* scales;      // [B, H, S_pad / 32]
+  const float* mean;  // [B, H, 128] subtracted (fp32) after the transform, or nullptr
+  int S, H, nblk, units;
+  float mult;         // c = scale * log2(e) for Q, 1 for K (x * 1.0f is exact)
+  RowXform xf;
+};
+
+// grid.x: ceil(max(units) / 4) workgroups of 4 waves; grid.y: 0 = Q, 1 = K.
+// One wave per (b, h, 32-row block): 32 rows x 256 B in, 4 KB of codes out, one scale.
+template <bool XF>
 __global__ void __launch_bounds__(256)
-quant_qk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                int8_t* __restrict__ q_i8, float* __restrict__ q_scale, int8_t* __restrict__ k_i8,
-                float* __restrict__ k_scale, int S, int H, int nblk, int units, float c,
-                uint32_t* __restrict__ amax_bits, int n_amax) {
+quant_qk_kernel(QuantSide qs, QuantSide ks, uint32_t* __restrict__ amax_bits, int n_amax) {
   // initialize the V absmax accumulator (flagged +0) for v_absmax_kernel, which runs
-  // next on the stream; the first ceil(n_amax / 256) workgroups of the Q half do it
+  // later on the stream; the first ceil(n_amax / 256) workgroups of the Q half do it
   {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (blockIdx.y == 0 && i < n_amax) amax_bits[i] = kAmaxFlag;
   }
-
-  const bool is_q = blockIdx.y == 0;
-  const uint16_t* x = is_q ? q : k;
-  int8_t* codes = is_q ? q_i8 : k_i8;
-  float* scales = is_q ? q_scale : k_scale;
-  const float mult = is_q ? c : 1.0f;  // x * 1.0f is exact
-
+  const QuantSide& a = blockIdx.y == 0 ? qs : ks;
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= units) return;
+  if (unit >= a.units) return;  // whole waves leave together
   const int lane = threadIdx.x & 63;
-  const int blk = unit % nblk;
-  const int bh = unit / nblk;
-  const int b = bh / H, h = bh - b * H;
-  const int64_t tok = (int64_t)H * kHeadDim;
-  const uint16_t* src = x + ((int64_t)b * S * H + h) * kHeadDim;
+  const int blk = unit % a.nblk;
+  const int bh = unit / a.nblk;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int64_t tok = (int64_t)a.H * kHeadDim;
+  const uint16_t* src = a.x + ((int64_t)b * a.S * a.H + h) * kHeadDim;
 
   // lane owns 8 channels (chunk lane & 15) of rows (lane >> 4) + 4 p, p = 0..7
   const int chunk = lane & 15;
   float y[8][8];
+  float mean[8];
+  if (a.mean) {
+    const float* m = a.mean + (int64_t)bh * kHeadDim + 8 * chunk;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mean[e] = m[e];
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int i = blk * 32 + (lane >> 4) + 4 * p;
     uint4 raw = uint4{0, 0, 0, 0};
-    if (i < S) raw = *(const uint4*)(src + i * tok + 8 * chunk);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    if (i < a.S) raw = *(const uint4*)(src + i * tok + 8 * chunk);
+    unpack_bf16x8(raw, y[p]);
+    if constexpr (XF) xform_fragment(y[p], chunk, i, i < a.S, a.xf);
+    if (a.mean && i < a.S) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      y[p][2 * e] = bf16_bits_to_f32(w[e] & 0xFFFFu) * mult;
-      y[p][2 * e + 1] = bf16_bits_to_f32(w[e] >> 16) * mult;
+      for (int e = 0; e < 8; ++e) y[p][e] = y[p][e] - mean[e];
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[p][e]));
+    for (int e = 0; e < 8; ++e) {
+      y[p][e] = y[p][e] * a.mult;
+      amax = fmaxf(amax, fabsf(y[p][e]));
+    }
   }
   amax = wave_max(amax);
   const float s = amax / 127.0f;
-  int8_t* dst = codes + ((int64_t)bh * nblk * 32 + blk * 32) * kHeadDim;
+  int8_t* dst = a.codes + ((int64_t)bh * a.nblk * 32 + blk * 32) * kHeadDim;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r = (lane >> 4) + 4 * p;
@@ -109,7 +193,105 @@ quant_qk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     *(uint2*)(dst + r * kHeadDim + 8 * chunk) = uint2{packed[0], packed[1]};
   }
-  if (lane == 0) scales[(int64_t)bh * nblk + blk] = s;
+  if (lane == 0) a.scales[(int64_t)bh * a.nblk + blk] = s;
+}
+
+// ---------------------------------------------------------------- transform alone
+// out = transform(x), BF16 [B, S, H, 128] -> BF16; same lanes as quant_qk_kernel.
+__global__ void __launch_bounds__(256)
+xform_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ out, int S, int H, int nblk,
+             int units, RowXform xf) {
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= units) return;
+  const int lane = threadIdx.x & 63;
+  const int blk = unit % nblk;
+  const int bh = unit / nblk;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t tok = (int64_t)H * kHeadDim;
+  const int64_t base = ((int64_t)b * S * H + h) * kHeadDim;
+  const int chunk = lane & 15;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int i = blk * 32 + (lane >> 4) + 4 * p;
+    uint4 raw = uint4{0, 0, 0, 0};
+    if (i < S) raw = *(const uint4*)(x + base + i * tok + 8 * chunk);
+    float y[8];
+    unpack_bf16x8(raw, y);
+    xform_fragment(y, chunk, i, i < S, xf);
+    if (i < S) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)y[2 * e]);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)y[2 * e + 1]);
+        w[e] = lo | (hi << 16);
+      }
+      *(uint4*)(out + base + i * tok + 8 * chunk) = uint4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------- K channel means (smoothing)
+// Per-(b, h, channel) mean of the (transformed) K values over the S tokens:
+// mean = fp32(fp64 sum / S).  k_colsum_kernel writes fp64 partial sums per token
+// range (no atomics, fixed order) to the workspace [B, nchunk, H, 128]; k_mean_kernel
+// adds them in range order.  Both sums are exact, hence order free, whenever the
+// values of a channel span less than 2^(45 - log2 S) in magnitude.
+// Grid and lanes as v_absmax_kernel: a workgroup covers 4 heads (64 lanes x 16 B) of
+// one token range; the 16 lanes of one head row sit together, as the transform needs.
+template <bool XF>
+__global__ void __launch_bounds__(256)
+k_colsum_kernel(const uint16_t* __restrict__ k, double* __restrict__ partial, int S, int H,
+                int tok_per_wg, int nchunk, int colblk, RowXform xf) {
+  __shared__ double red[4][64][8];
+  const int rng = blockIdx.x % nchunk;
+  const int bc = blockIdx.x / nchunk;
+  const int b = bc / colblk, cb = bc - b * colblk;
+  const int ncol = H * 16;
+  const int col = cb * 64 + (threadIdx.x & 63);
+  const bool col_ok = col < ncol;  // a whole head (16 lanes) is in or out
+  const int wv = threadIdx.x >> 6;
+  const int chunk = threadIdx.x & 15;
+  const int j0 = rng * tok_per_wg;
+  const int j1 = min(j0 + tok_per_wg, S);
+  const int64_t tok = (int64_t)H * kHeadDim;
+  const uint16_t* src = k + (int64_t)b * S * tok + 8 * (int64_t)(col_ok ? col : 0);
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = j0 + wv; j < j1; j += 4) {  // wave-uniform trip count
+    uint4 raw = uint4{0, 0, 0, 0};
+    if (col_ok) raw = *(const uint4*)(src + j * tok);
+    float y[8];
+    unpack_bf16x8(raw, y);
+    if constexpr (XF) xform_fragment(y, chunk, j, col_ok, xf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (double)y[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[wv][threadIdx.x & 63][e] = acc[e];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = threadIdx.x + 256 * r;
+    const int c = idx >> 3, e = idx & 7;
+    const int gcol = cb * 64 + c;
+    if (gcol < ncol)
+      partial[((int64_t)b * nchunk + rng) * H * kHeadDim + 8 * gcol + e] =
+          (red[0][c][e] + red[1][c][e]) + (red[2][c][e] + red[3][c][e]);
+  }
+}
+
+// grid: ceil(B * H * 128 / 256); one thread per (b, h, channel).
+__global__ void __launch_bounds__(256)
+k_mean_kernel(const double* __restrict__ partial, float* __restrict__ k_mean, int S, int H,
+              int nchunk, int n) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int hc = H * kHeadDim;
+  const int b = idx / hc, r = idx - b * hc;
+  const double* p = partial + (int64_t)b * nchunk * hc + r;
+  double s = 0.0;
+  for (int c = 0; c < nchunk; ++c) s += p[(int64_t)c * hc];
+  k_mean[idx] = (float)(s / (double)S);
 }
 
 // ---------------------------------------------------------------- V absmax
@@ -240,29 +422,82 @@ v_quant_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits,
 
 }  // namespace prep
 
-hipError_t launch_sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8,
-                               float* q_scale, int8_t* k_i8, float* k_scale, uint8_t* v_fp8,
-                               float* v_scale, int B, int S, int H, int S_pad, float c,
+namespace {
+
+// Token ranges of v_absmax_kernel and k_colsum_kernel: about 1000 workgroups
+// whatever the shape, ranges a multiple of 16 tokens.
+struct Chunking {
+  int tok_per_wg, nchunk, colblk;
+};
+Chunking chunking(int B, int S, int H) {
+  Chunking c;
+  c.colblk = (H * 16 + 63) / 64;
+  int t = (int)(((int64_t)S * c.colblk * B + 1023) / 1024);
+  t = (t + 15) / 16 * 16;
+  c.tok_per_wg = t < 16 ? 16 : t;
+  c.nchunk = (S + c.tok_per_wg - 1) / c.tok_per_wg;
+  return c;
+}
+
+prep::RowXform row_xform(const void* norm_w, float eps, const void* cos_t, const void* sin_t,
+                         int rope_dim) {
+  return prep::RowXform{(const uint16_t*)norm_w, eps, (const uint16_t*)cos_t, (const uint16_t*)sin_t,
+                        rope_dim};
+}
+
+}  // namespace
+
+size_t sage_workspace_bytes(int B, int S_kv, int H_kv) {
+  const Chunking ch = chunking(B, S_kv, H_kv);
+  return (size_t)B * ch.nchunk * H_kv * kHeadDim * sizeof(double);
+}
+
+hipError_t launch_sage_prepare(const PrepareArgs& a, hipStream_t stream) {
+  const int S_q_pad = (a.S_q + 255) / 256 * 256, S_kv_pad = (a.S_kv + 255) / 256 * 256;
+  const bool xq = a.q_norm_w || a.rope_dim, xk = a.k_norm_w || a.rope_dim;
+  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(a.v_scale);
+  const Chunking ch = chunking(a.B, a.S_kv, a.H_kv);
+  hipError_t e;
+  if (a.k_mean) {  // K smoothing: channel means of the (transformed) K first
+    double* partial = reinterpret_cast<double*>(a.workspace);
+    const prep::RowXform kx = row_xform(a.k_norm_w, a.eps, a.rope_cos, a.rope_sin, a.rope_dim);
+    const dim3 grid(a.B * ch.colblk * ch.nchunk);
+    e = xk ? launch(prep::k_colsum_kernel<true>, grid, dim3(256), stream, (const uint16_t*)a.k, partial,
+                    a.S_kv, a.H_kv, ch.tok_per_wg, ch.nchunk, ch.colblk, kx)
+           : launch(prep::k_colsum_kernel<false>, grid, dim3(256), stream, (const uint16_t*)a.k, partial,
+                    a.S_kv, a.H_kv, ch.tok_per_wg, ch.nchunk, ch.colblk, kx);
+    if (e != hipSuccess) return e;
+    const int n = a.B * a.H_kv * kHeadDim;
+    e = launch(prep::k_mean_kernel, dim3((n + 255) / 256), dim3(256), stream, (const double*)partial,
+               a.k_mean, a.S_kv, a.H_kv, ch.nchunk, n);
+    if (e != hipSuccess) return e;
+  }
+  prep::QuantSide qs{(const uint16_t*)a.q, a.q_i8, a.q_scale, nullptr, a.S_q, a.H, S_q_pad / 32,
+                     a.B * a.H * (S_q_pad / 32), a.c,
+                     row_xform(a.q_norm_w, a.eps, a.rope_cos, a.rope_sin, a.rope_dim)};
+  prep::QuantSide ks{(const uint16_t*)a.k, a.k_i8, a.k_scale, a.k_mean, a.S_kv, a.H_kv, S_kv_pad / 32,
+                     a.B * a.H_kv * (S_kv_pad / 32), 1.0f,
+                     row_xform(a.k_norm_w, a.eps, a.rope_cos, a.rope_sin, a.rope_dim)};
+  const int units = qs.units > ks.units ? qs.units : ks.units;
+  const int n_amax = a.B * a.H_kv * kHeadDim;  // <= 64 * qs.units: the Q half covers it
+  const dim3 qgrid((units + 3) / 4, 2);
+  e = (xq || xk) ? launch(prep::quant_qk_kernel<true>, qgrid, dim3(256), stream, qs, ks, amax_bits, n_amax)
+                 : launch(prep::quant_qk_kernel<false>, qgrid, dim3(256), stream, qs, ks, amax_bits, n_amax);
+  if (e != hipSuccess) return e;
+  e = launch(prep::v_absmax_kernel, dim3(a.B * ch.colblk * ch.nchunk), dim3(256), stream,
+             (const uint16_t*)a.v, amax_bits, a.S_kv, a.H_kv, ch.tok_per_wg, ch.nchunk, ch.colblk);
+  if (e != hipSuccess) return e;
+  return launch(prep::v_quant_kernel, dim3(a.B * a.H_kv * (S_kv_pad / prep::kVTok)), dim3(256), stream,
+                (const uint16_t*)a.v, amax_bits, a.v_fp8, a.S_kv, a.H_kv, S_kv_pad);
+}
+
+hipError_t launch_qk_norm_rope(const void* x, void* out, int B, int S, int H, const void* norm_w,
+                               float eps, const void* cos_t, const void* sin_t, int rope_dim,
                                hipStream_t stream) {
-  const int nblk = S_pad / 32;
+  const int nblk = (S + 31) / 32;
   const int units = B * H * nblk;
-  const int nscale = B * H * kHeadDim;  // <= units: the Q half of quant_qk covers it
-  uint32_t* amax_bits = reinterpret_cast<uint32_t*>(v_scale);
-  hipError_t e = launch(prep::quant_qk_kernel, dim3((units + 3) / 4, 2), dim3(256), stream,
-                        (const uint16_t*)q, (const uint16_t*)k, q_i8, q_scale, k_i8, k_scale, S, H,
-                        nblk, units, c, amax_bits, nscale);
-  if (e != hipSuccess) return e;
-  // V absmax: about 1000 workgroups whatever the shape, token ranges a multiple of 16
-  const int colblk = (H * 16 + 63) / 64;
-  int tok_per_wg = (int)(((int64_t)S * colblk * B + 1023) / 1024);
-  tok_per_wg = (tok_per_wg + 15) / 16 * 16;
-  if (tok_per_wg < 16) tok_per_wg = 16;
-  const int nchunk = (S + tok_per_wg - 1) / tok_per_wg;
-  e = launch(prep::v_absmax_kernel, dim3(B * colblk * nchunk), dim3(256), stream, (const uint16_t*)v,
-             amax_bits, S, H, tok_per_wg, nchunk, colblk);
-  if (e != hipSuccess) return e;
-  return launch(prep::v_quant_kernel, dim3(B * H * (S_pad / prep::kVTok)), dim3(256), stream,
-                (const uint16_t*)v, amax_bits, v_fp8, S, H, S_pad);
+  return launch(prep::xform_kernel, dim3((units + 3) / 4), dim3(256), stream, (const uint16_t*)x,
+                (uint16_t*)out, S, H, nblk, units, row_xform(norm_w, eps, cos_t, sin_t, rope_dim));
 }
 
 }  // namespace ditattn

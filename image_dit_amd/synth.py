@@ -82,6 +82,23 @@ def make_qkv_device(B, S, H, device, D=HEAD_DIM, seed=0, k_bias_std=0.0):
     return q, k.to(torch.bfloat16), v
 
 
+def make_norm_weight(D=HEAD_DIM, seed=0):
+    """A BF16 RMSNorm weight [D]: 1 + 0.25 * N(0, 1), seeded."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    return (1.0 + 0.25 * torch.randn(D, generator=g)).to(torch.bfloat16)
+
+
+def make_rope_tables(S, rope_dim, base=10000.0):
+    """BF16 cos/sin tables [S, rope_dim] of the rotate-half form: angle
+    pos * base^(-i / (rope_dim / 2)) for i < rope_dim / 2, the two halves
+    equal; computed in float64 and rounded to BF16 once."""
+    half = rope_dim // 2
+    inv = 1.0 / base ** (torch.arange(half, dtype=torch.float64) / half)
+    ang = torch.arange(S, dtype=torch.float64)[:, None] * inv[None, :]
+    ang = torch.cat((ang, ang), dim=-1)
+    return torch.cos(ang).to(torch.bfloat16), torch.sin(ang).to(torch.bfloat16)
+
+
 def workload_qkv(w: Workload):
     return make_qkv(w.B, w.S, w.H, w.D, seed=w.seed, k_bias_std=w.k_bias_std)
 

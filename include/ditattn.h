@@ -44,6 +44,7 @@
 #ifndef DITATTN_H
 #define DITATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -54,7 +55,7 @@ extern "C" {
 struct ihipStream_t;
 typedef struct ihipStream_t* hipStream_t;
 
-#define DITATTN_ABI_VERSION 1
+#define DITATTN_ABI_VERSION 2
 
 /* Size limits (see the conventions above). */
 #define DITATTN_MAX_HEADS 65536
@@ -62,8 +63,9 @@ typedef struct ihipStream_t* hipStream_t;
 
 /* Status codes. */
 #define DITATTN_OK 0
-#define DITATTN_EINVAL (-1)       /* B, S or H < 1, null pointer, scale not finite or <= 0, output aliasing an input */
-#define DITATTN_EUNSUPPORTED (-2) /* D != 128 */
+#define DITATTN_EINVAL (-1)       /* a size < 1, null pointer, scale not finite or <= 0, bad eps,
+                                     H not a multiple of H_kv, short workspace, output aliasing an input */
+#define DITATTN_EUNSUPPORTED (-2) /* D != 128, rope_dim not 0/32/64/96/128 */
 #define DITATTN_EALIGN (-3)       /* a pointer is not 16-byte aligned */
 #define DITATTN_EOVERFLOW (-4)    /* a byte size or the grid exceeds what the kernels index */
 #define DITATTN_EHIP (-5)         /* the HIP runtime rejected a launch */
@@ -126,6 +128,67 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, i
 int sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8, float* q_scale,
                  int8_t* k_i8, float* k_scale, uint8_t* v_fp8, float* v_scale, int B, int S,
                  int H, int D, float scale, hipStream_t stream);
+
+/*
+ * sage_prepare_ex -- sage_prepare with the optional Q/K row transform, K
+ * smoothing and cross-attention / grouped-query shapes.
+ *
+ * Shapes: q is BF16 [B, S_q, H, 128]; k, v are BF16 [B, S_kv, H_kv, 128] with
+ * H a multiple of H_kv.  Outputs as sage_prepare with S_q for the Q side and
+ * S_kv, H_kv for the K and V sides: q_i8 [B, H, S_q_pad, 128], q_scale
+ * [B, H, S_q_pad / 32], k_i8 [B, H_kv, S_kv_pad, 128], k_scale
+ * [B, H_kv, S_kv_pad / 32], v_fp8 [B, H_kv, 128, S_kv_pad], v_scale [B, H_kv, 128].
+ *
+ * Row transform ([SAGE] first commit and "Technical Details": optional QK
+ * RMSNorm and rotate-half RoPE, rounded like the eager PyTorch BF16
+ * sequence), applied to each 128-channel Q and K row before quantization:
+ *   q_norm_w, k_norm_w : BF16 [128] RMSNorm weights, or NULL (no RMSNorm on that side)
+ *       n = bf16(x * r), r = 1 / sqrt(sum(x^2) / 128 + norm_eps) in fp32 (the sum
+ *       a pairwise tree over the channels in index order), y = bf16(n * w)
+ *   rope_dim : 0 (no RoPE), 32, 64, 96 or 128
+ *   rope_cos, rope_sin : BF16 [>= max(S_q, S_kv), rope_dim], row = token position
+ *       out[c] = bf16(bf16(y[c] * cos[c]) + bf16(rot[c] * sin[c])) for c < rope_dim,
+ *       rot[c] = -y[c + rope_dim/2] below rope_dim/2, y[c - rope_dim/2] above
+ *   norm_eps : finite, >= 0
+ * RMSNorm comes first, then RoPE, then (for Q) the multiply by scale * log2(e).
+ * The result equals qk_norm_rope_bf16 followed by sage_prepare, bit for bit.
+ *
+ * K smoothing ("Kernel acceleration: attention, compilation and fusion",
+ * section "SageAttention: quantizing attention too": subtracting K's mean over
+ * the tokens before quantizing leaves attention unchanged, since it shifts every
+ * score of a query row by the same amount):
+ *   k_mean : fp32 [B, H_kv, 128] output, or NULL (no smoothing).  When given,
+ *       k_mean = fp32(sum_j y_j / S_kv) with the sum over the (transformed) K
+ *       values in fp64, and K is quantized as fp32(y) - k_mean.
+ *   workspace, workspace_bytes : device scratch of at least
+ *       ditattn_sage_workspace_size(B, S_kv, H_kv) bytes when k_mean is given
+ *       (ignored otherwise); contents on entry do not matter.
+ * The fp64 channel sums are exact (so the mean is independent of the
+ * summation order) when the values of a channel span less than
+ * 2^(45 - ceil(log2 S_kv)) in magnitude.
+ * Outputs, k_mean and workspace must not overlap each other or any input.
+ */
+int sage_prepare_ex(const void* q, const void* k, const void* v, int8_t* q_i8, float* q_scale,
+                    int8_t* k_i8, float* k_scale, uint8_t* v_fp8, float* v_scale, int B, int S_q,
+                    int S_kv, int H, int H_kv, int D, float scale, const void* q_norm_w,
+                    const void* k_norm_w, float norm_eps, const void* rope_cos,
+                    const void* rope_sin, int rope_dim, float* k_mean, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes sage_prepare_ex needs for K smoothing at these sizes (0 for
+ * sizes it rejects).  Touches no GPU. */
+size_t ditattn_sage_workspace_size(int B, int S_kv, int H_kv);
+
+/*
+ * qk_norm_rope_bf16 -- the row transform of sage_prepare_ex alone, BF16 in and
+ * out: out = RoPE(RMSNorm(x)) per [b, s, h] row with the same arithmetic and
+ * arguments (norm_w NULL: no RMSNorm; rope_dim 0: no RoPE; tables
+ * [>= S, rope_dim]).  x, out: BF16 [B, S, H, 128]; out == x (in place) is
+ * allowed, any other overlap is not.
+ */
+int qk_norm_rope_bf16(const void* x, void* out, int B, int S, int H, int D, const void* norm_w,
+                      float norm_eps, const void* rope_cos, const void* rope_sin, int rope_dim,
+                      hipStream_t stream);
 
 /*
  * sage_attn_fwd -- the quantized forward on tensors written by sage_prepare

@@ -58,11 +58,14 @@ def _lib():
         lib.oracle_sage_padded_len.restype = ci
         lib.oracle_quant_qk.argtypes = [u16p, ci, ci, ci, ci, cf, ci, i8p, f32p]
         lib.oracle_quant_v.argtypes = [u16p, ci, ci, ci, ci, ci, u8p, f32p]
+        lib.oracle_quant_qk_mean.argtypes = [u16p, ci, ci, ci, ci, cf, ci, f32p, i8p, f32p]
+        lib.oracle_channel_mean.argtypes = [u16p, ci, ci, ci, ci, f32p]
         lib.oracle_f32_to_bf16.argtypes = [cf]
         lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
         lib.oracle_qk_norm_rope.argtypes = [u16p, ci, ci, ci, ci, u16p, cf, u16p, u16p, ci, u16p]
         for name in ("oracle_softmax_row", "oracle_attn_rows", "oracle_attn_blocked",
-                     "oracle_quant_qk", "oracle_quant_v", "oracle_qk_norm_rope"):
+                     "oracle_quant_qk", "oracle_quant_v", "oracle_qk_norm_rope",
+                     "oracle_quant_qk_mean", "oracle_channel_mean"):
             getattr(lib, name).restype = ci
         _LIB = lib
     return _LIB
@@ -158,17 +161,34 @@ def sage_padded_len(S):
     return int(_lib().oracle_sage_padded_len(int(S)))
 
 
-def quant_qk(x, mult):
-    """INT8 block quantization: codes [B, H, S_pad, D] int8, scales [B, H, S_pad/32] fp32."""
+def quant_qk(x, mult, mean=None):
+    """INT8 block quantization: codes [B, H, S_pad, D] int8, scales [B, H, S_pad/32] fp32.
+    With mean (fp32 [B, H, D]) the values quantized are (fp32(x) - mean) * mult."""
     x = _bits(x)
     B, S, H, D = x.shape
     S_pad = sage_padded_len(S)
     codes = np.empty((B, H, S_pad, D), dtype=np.int8)
     scales = np.empty((B, H, S_pad // 32), dtype=np.float32)
-    _check(_lib().oracle_quant_qk(_ptr(x, ctypes.c_uint16), B, S, H, D, float(mult), S_pad,
-                                  _ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_float)),
-           "oracle_quant_qk")
+    if mean is None:
+        st = _lib().oracle_quant_qk(_ptr(x, ctypes.c_uint16), B, S, H, D, float(mult), S_pad,
+                                    _ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_float))
+    else:
+        mean = np.ascontiguousarray(mean, dtype=np.float32).reshape(B, H, D)
+        st = _lib().oracle_quant_qk_mean(_ptr(x, ctypes.c_uint16), B, S, H, D, float(mult), S_pad,
+                                         _ptr(mean, ctypes.c_float), _ptr(codes, ctypes.c_int8),
+                                         _ptr(scales, ctypes.c_float))
+    _check(st, "oracle_quant_qk")
     return codes, scales
+
+
+def channel_mean(x):
+    """fp32(fp64 sum over tokens / S) per (b, h, channel): fp32 [B, H, D]."""
+    x = _bits(x)
+    B, S, H, D = x.shape
+    mean = np.empty((B, H, D), dtype=np.float32)
+    _check(_lib().oracle_channel_mean(_ptr(x, ctypes.c_uint16), B, S, H, D, _ptr(mean, ctypes.c_float)),
+           "oracle_channel_mean")
+    return mean
 
 
 def quant_v(v):
@@ -221,10 +241,20 @@ def qk_norm_rope(x, norm_w=None, eps=1e-6, cos=None, sin=None, rope_dim=0):
     return out
 
 
-def sage_prepare_fused(q, k, v, scale, q_norm_w=None, k_norm_w=None, eps=1e-6, cos=None,
-                       sin=None, rope_dim=0):
-    """Prepare with the optional Q/K transform: by definition the quantizer
-    applied to qk_norm_rope(q) and qk_norm_rope(k)."""
-    qt = qk_norm_rope(q, q_norm_w, eps, cos, sin, rope_dim)
-    kt = qk_norm_rope(k, k_norm_w, eps, cos, sin, rope_dim)
-    return sage_prepare(qt, kt, v, scale)
+def sage_prepare_ex(q, k, v, scale, q_norm_w=None, k_norm_w=None, eps=1e-6, cos=None,
+                    sin=None, rope_dim=0, smooth_k=False):
+    """The prepare stage with its options, by definition:
+    Q' = qk_norm_rope(q), K' = qk_norm_rope(k) (each side's transform only when
+    asked for), then the quantizer on Q', K' (minus K''s channel mean when
+    smooth_k) and V.  Q and K/V may differ in tokens and heads.  Returns the
+    six prepared arrays, plus the K channel mean when smooth_k."""
+    xq = q_norm_w is not None or rope_dim
+    xk = k_norm_w is not None or rope_dim
+    qt = qk_norm_rope(q, q_norm_w, eps, cos, sin, rope_dim) if xq else _bits(q)
+    kt = qk_norm_rope(k, k_norm_w, eps, cos, sin, rope_dim) if xk else _bits(k)
+    mean = channel_mean(kt) if smooth_k else None
+    qc, qs = quant_qk(qt, q_multiplier(scale))
+    kc, ks = quant_qk(kt, 1.0, mean)
+    vc, vs = quant_v(v)
+    out = (qc, qs, kc, ks, vc, vs)
+    return out + (mean,) if smooth_k else out

@@ -319,8 +319,23 @@ int oracle_sage_padded_len(int S) { return (S + 255) / 256 * 256; }
  *   code = clamp(rint(y / s), -127, 127), or 0 when s == 0
  * codes: int8 [B, H, S_pad, D]; scales: fp32 [B, H, S_pad / 32].
  */
+int oracle_quant_qk_mean(const uint16_t* x, int B, int S, int H, int D, float mult, int S_pad,
+                         const float* mean, int8_t* codes, float* scales);
+
 int oracle_quant_qk(const uint16_t* x, int B, int S, int H, int D, float mult, int S_pad,
                     int8_t* codes, float* scales) {
+  return oracle_quant_qk_mean(x, B, S, H, D, mult, S_pad, NULL, codes, scales);
+}
+
+/*
+ * As oracle_quant_qk, with y = (fp32(x) - mean[b, h, d]) * mult when mean is not
+ * NULL (mean: fp32 [B, H, D]; the subtraction is one fp32 operation).  This is
+ * the smoothed K of the prepare stage ("Kernel acceleration: attention,
+ * compilation and fusion", section "SageAttention: quantizing attention too":
+ * K minus its mean over the tokens gives the same attention).
+ */
+int oracle_quant_qk_mean(const uint16_t* x, int B, int S, int H, int D, float mult, int S_pad,
+                         const float* mean, int8_t* codes, float* scales) {
   if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || S_pad < S || S_pad % 32 != 0) return ORACLE_EINVAL;
   const int nblk = S_pad / 32;
   int status = ORACLE_OK;
@@ -331,10 +346,13 @@ int oracle_quant_qk(const uint16_t* x, int B, int S, int H, int D, float mult, i
       for (int blk = 0; blk < nblk; ++blk) {
         const int i0 = blk * 32;
         const int i1 = (i0 + 32 < S) ? i0 + 32 : S;
+        const float* mu = mean ? mean + ((int64_t)b * H + h) * D : NULL;
         float amax = 0.0f;
         for (int i = i0; i < i1; ++i)
           for (int d = 0; d < D; ++d) {
-            const float y = bf16_to_f32(x[idx_bshd(b, i, h, d, S, H, D)]) * mult;
+            float y = bf16_to_f32(x[idx_bshd(b, i, h, d, S, H, D)]);
+            if (mu) y = y - mu[d];
+            y = y * mult;
             if (!isfinite(y)) {
 #pragma omp atomic write
               status = ORACLE_ENONFINITE;
@@ -348,7 +366,9 @@ int oracle_quant_qk(const uint16_t* x, int B, int S, int H, int D, float mult, i
           for (int d = 0; d < D; ++d) {
             int8_t code = 0;
             if (i < i1 && s != 0.0f) {
-              const float y = bf16_to_f32(x[idx_bshd(b, i, h, d, S, H, D)]) * mult;
+              float y = bf16_to_f32(x[idx_bshd(b, i, h, d, S, H, D)]);
+              if (mu) y = y - mu[d];
+              y = y * mult;
               float r = rintf(y / s);
               if (r > 127.0f) r = 127.0f;
               if (r < -127.0f) r = -127.0f;
@@ -457,6 +477,24 @@ int oracle_qk_norm_rope(const uint16_t* x, int B, int S, int H, int D, const uin
           for (int c = 0; c < rope_dim; ++c) y[c] = z[c];
         }
         for (int d = 0; d < D; ++d) out[idx_bshd(b, i, h, d, S, H, D)] = oracle_f32_to_bf16(y[d]);
+      }
+  return ORACLE_OK;
+}
+
+/*
+ * Channel means for K smoothing: mean[b, h, d] = fp32( (sum over j < S of
+ * fp64(x[b, j, h, d])) / S ), the sum taken in token order in fp64 and the
+ * quotient rounded to fp32.  mean: fp32 [B, H, D].
+ */
+int oracle_channel_mean(const uint16_t* x, int B, int S, int H, int D, float* mean) {
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0) return ORACLE_EINVAL;
+#pragma omp parallel for collapse(3) schedule(static)
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h)
+      for (int d = 0; d < D; ++d) {
+        double s = 0.0;
+        for (int j = 0; j < S; ++j) s += (double)bf16_to_f32(x[idx_bshd(b, j, h, d, S, H, D)]);
+        mean[((int64_t)b * H + h) * D + d] = (float)(s / (double)S);
       }
   return ORACLE_OK;
 }

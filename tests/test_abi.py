@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("attn_fwd_bf16", "sage_prepare", "sage_attn_fwd", "ditattn_sage_padded_len",
-              "ditattn_status_string", "ditattn_abi_version", "ditattn_check_shape"):
+              "ditattn_status_string", "ditattn_abi_version", "ditattn_check_shape",
+              "sage_prepare_ex", "qk_norm_rope_bf16", "ditattn_sage_workspace_size"):
         assert n in names
 
 
@@ -55,7 +56,7 @@ def test_library_links_only_the_hip_runtime():
 
 
 def test_abi_version_and_padded_len(lib):
-    assert lib.ditattn_abi_version() == 1
+    assert lib.ditattn_abi_version() == 2
     assert [lib.ditattn_sage_padded_len(s) for s in (1, 256, 257, 4608, 76112)] == [256, 256, 512, 4608, 76288]
     assert lib.ditattn_sage_padded_len(0) == -1
     assert lib.ditattn_sage_padded_len(2**31 - 1) == -1
@@ -226,3 +227,64 @@ def test_binding_rejects_wrong_outputs_before_any_call(monkeypatch):
     with pytest.raises(ValueError):
         mod.sage_prepare(q, q, q, 0.088, out=tuple(good[:5]))
     assert calls == []  # nothing reached the library
+
+
+# ---------------------------------------------------------------- sage_prepare_ex / qk_norm_rope_bf16
+def prep_ex_call(lib, override=None, B=1, S_q=100, S_kv=100, H=2, H_kv=2, D=128, scale=0.088,
+                 norm=(None, None), eps=1e-6, rope=(None, None), rope_dim=0, k_mean=None, ws=None,
+                 ws_bytes=0):
+    ptrs = [GOOD * 2 ** (20 + i) for i in range(9)]
+    for i, val in (override or {}).items():
+        ptrs[i] = val
+    vp = ctypes.c_void_p
+    return lib.sage_prepare_ex(*[vp(p) for p in ptrs], B, S_q, S_kv, H, H_kv, D, ctypes.c_float(scale),
+                               vp(norm[0]), vp(norm[1]), ctypes.c_float(eps), vp(rope[0]), vp(rope[1]),
+                               rope_dim, vp(k_mean), vp(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_sage_prepare_ex_rejects(lib):
+    W = GOOD * 2 ** 40  # far from every other fake buffer
+    assert prep_ex_call(lib, H=3, H_kv=2) == EINVAL  # H not a multiple of H_kv
+    assert prep_ex_call(lib, S_kv=0) == EINVAL
+    assert prep_ex_call(lib, eps=-1.0) == EINVAL
+    assert prep_ex_call(lib, eps=float("inf")) == EINVAL
+    for rd in (16, 48, 100, 256):
+        assert prep_ex_call(lib, rope_dim=rd, rope=(W, W + 2 ** 24)) == EUNSUPPORTED
+    assert prep_ex_call(lib, rope_dim=64, rope=(W, None)) == EINVAL
+    assert prep_ex_call(lib, rope_dim=64, rope=(W + 4, W + 2 ** 24)) == EALIGN
+    assert prep_ex_call(lib, norm=(W + 2, None)) == EALIGN
+    # smoothing needs a workspace of the size the library states
+    need = lib.ditattn_sage_workspace_size(1, 100, 2)
+    assert need > 0
+    assert prep_ex_call(lib, k_mean=W) == EINVAL
+    assert prep_ex_call(lib, k_mean=W, ws=W + 2 ** 24, ws_bytes=need - 1) == EINVAL
+    assert prep_ex_call(lib, k_mean=W + 8, ws=W + 2 ** 24, ws_bytes=need) == EALIGN
+    # k_mean over the workspace, workspace over v
+    assert prep_ex_call(lib, k_mean=W, ws=W, ws_bytes=need) == EINVAL
+    assert prep_ex_call(lib, k_mean=W, ws=GOOD * 2 ** 22, ws_bytes=need) == EINVAL
+    # RoPE tables under an output
+    assert prep_ex_call(lib, rope_dim=32, rope=(GOOD * 2 ** 23, W)) == EINVAL
+    assert prep_ex_call(lib, D=64) == EUNSUPPORTED
+
+
+def test_workspace_size_is_positive_and_bounded(lib):
+    lib.ditattn_sage_workspace_size.restype = ctypes.c_size_t
+    for B, S, H in ((1, 256, 2), (1, 4608, 24), (1, 76112, 40), (4, 300, 5)):
+        n = lib.ditattn_sage_workspace_size(B, S, H)
+        assert 0 < n <= max(8 << 20, B * H * 1024 * 2)
+    assert lib.ditattn_sage_workspace_size(0, 10, 1) == 0
+
+
+def test_qk_norm_rope_rejects(lib):
+    vp = ctypes.c_void_p
+    W = GOOD * 2 ** 40
+
+    def call(x=GOOD, out=GOOD * 2 ** 30, S=64, H=2, D=128, w=None, eps=1e-6, rope=(None, None), rd=0):
+        return lib.qk_norm_rope_bf16(vp(x), vp(out), 1, S, H, D, vp(w), ctypes.c_float(eps), vp(rope[0]),
+                                     vp(rope[1]), rd, None)
+    assert call(x=0) == EINVAL
+    assert call(D=256) == EUNSUPPORTED
+    assert call(rd=40, rope=(W, W + 2 ** 24)) == EUNSUPPORTED
+    assert call(eps=float("nan"), w=W) == EINVAL
+    assert call(out=GOOD + 256) == EINVAL  # partial overlap; exact in-place is allowed
+    assert call(w=GOOD * 2 ** 30 + 1024) == EINVAL  # weight inside the output

@@ -454,3 +454,51 @@ def test_rope_matches_the_rotation_in_fp64():
     err = (got[..., :rd] - exp).abs().max().item()
     assert err <= 3 * 2.0 ** -8 * xd.abs().max().item(), err
     assert torch.equal(got[..., rd:], xd[..., rd:])
+
+
+# --------------------------------------------------------------------------
+# K smoothing ("Kernel acceleration: attention, compilation and fusion",
+# section "SageAttention: quantizing attention too")
+# --------------------------------------------------------------------------
+
+def test_channel_mean_is_the_rounded_exact_mean():
+    # fp32(fp64(exact sum) / S): math.fsum gives the exactly rounded sum
+    B, S, H, D = 2, 777, 3, 128
+    _, k, _ = synth.make_qkv(B, S, H, D, seed=21, k_bias_std=2.0)
+    got = oracle.channel_mean(k)
+    kd = k.double().numpy()
+    for b, h, d in [(0, 0, 0), (1, 2, 127), (0, 1, 64), (1, 0, 5)]:
+        exact = math.fsum(kd[b, :, h, d].tolist())
+        assert got[b, h, d] == np.float32(exact / S)
+    ref = np.float32(kd.sum(axis=1) / S)  # [B, H, D]; the fp64 sum is exact here, any order agrees
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_smoothing_constant_keys_gives_zero_codes():
+    # every key equal to u: the mean is u exactly and the smoothed K is 0
+    B, S, H, D = 1, 96, 2, 128
+    u = torch.randn((1, 1, H, D), generator=torch.Generator().manual_seed(3))
+    k = bf16(u.expand(B, S, H, D).contiguous())
+    mean = oracle.channel_mean(k)
+    assert np.array_equal(mean, k[0, 0].float().numpy()[None])
+    codes, scales = oracle.quant_qk(k, 1.0, mean)
+    assert not codes.any() and not scales.any()
+
+
+def test_smoothed_quant_matches_torch_vectorized():
+    B, S, H, D = 1, 100, 2, 128
+    _, k, _ = synth.make_qkv(B, S, H, D, seed=22, k_bias_std=2.0)
+    mean = oracle.channel_mean(k)
+    codes, scales = oracle.quant_qk(k, 1.0, mean)
+    y = k.float().permute(0, 2, 1, 3) - torch.from_numpy(mean)[:, :, None, :]  # [B, H, S, D]
+    Sp = oracle.sage_padded_len(S)
+    y = torch.nn.functional.pad(y, (0, 0, 0, Sp - S)).reshape(B, H, Sp // 32, 32 * D)
+    amax = y.abs().amax(-1)
+    s = amax / 127.0
+    ref = torch.where(s[..., None] > 0, torch.round(y / s[..., None]), torch.zeros(()))
+    ref = ref.clamp(-127, 127).to(torch.int8).reshape(B, H, Sp, D)
+    assert torch.equal(torch.from_numpy(scales), s)
+    assert torch.equal(torch.from_numpy(codes), ref)
+    # smoothing shrinks the block scales of a K with per-channel bias
+    _, plain = oracle.quant_qk(k, 1.0)
+    assert float(scales[:, :, : S // 32].mean()) < 0.7 * float(plain[:, :, : S // 32].mean())
