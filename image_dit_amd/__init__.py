@@ -18,8 +18,9 @@ import ctypes
 import os
 
 __all__ = ["DitAttnError", "load", "abi_version", "sage_padded_len", "sage_workspace_size",
-           "attn_fwd_bf16", "sage_prepare", "sage_prepare_ex", "qk_norm_rope_bf16", "sage_attn_fwd",
-           "sage_attention", "HEAD_DIM", "LIB_PATH"]
+           "attn_fwd_bf16", "attn_fwd_bf16_ex", "sage_prepare", "sage_prepare_ex",
+           "qk_norm_rope_bf16", "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attention",
+           "sage_attention_ex", "HEAD_DIM", "LIB_PATH"]
 
 HEAD_DIM = 128
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
@@ -55,10 +56,12 @@ def load(path=None):
     lib.sage_prepare_ex.argtypes = ([vp] * 9 + [ci] * 6 + [cf, vp, vp, cf, vp, vp, ci, vp, vp,
                                                           ctypes.c_size_t, vp])
     lib.qk_norm_rope_bf16.argtypes = [vp, vp, ci, ci, ci, ci, vp, cf, vp, vp, ci, vp]
+    lib.attn_fwd_bf16_ex.argtypes = [vp, vp, vp, vp] + [ci] * 6 + [cf, ci, ci, vp]
+    lib.sage_attn_fwd_ex.argtypes = [vp] * 7 + [ci] * 6 + [cf, ci, ci, vp]
     lib.ditattn_sage_workspace_size.argtypes = [ci, ci, ci]
     lib.ditattn_sage_workspace_size.restype = ctypes.c_size_t
     for name in ("attn_fwd_bf16", "sage_prepare", "sage_attn_fwd", "sage_prepare_ex",
-                 "qk_norm_rope_bf16"):
+                 "qk_norm_rope_bf16", "attn_fwd_bf16_ex", "sage_attn_fwd_ex"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -166,6 +169,31 @@ def attn_fwd_bf16(q, k, v, scale, out=None, stream=None):
     st = lib.attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, H, D, float(scale),
                            _stream_handle(stream))
     _status(lib, "attn_fwd_bf16", st)
+    return out
+
+
+def attn_fwd_bf16_ex(q, k, v, scale, window=(-1, -1), out=None, stream=None):
+    """BF16 attention with q [B, S_q, H, 128], k and v [B, S_kv, H_kv, 128] (H a
+    multiple of H_kv) and a key window (window_left, window_right): query i sees
+    key j when i + off - wl <= j <= i + off + wr, off = S_kv - S_q, -1 meaning no
+    bound on that side ((-1, 0) is causal).  Rows that see no key are zeros."""
+    import torch
+    lib = load()
+    B, S_q, H, D = _dims(q)
+    _, S_kv, H_kv, _ = _dims(k)
+    _check_bshd("q", q, torch.bfloat16)
+    for name, t in (("k", k), ("v", v)):
+        _check_bshd(name, t, torch.bfloat16)
+        if tuple(t.shape) != (B, S_kv, H_kv, D):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S_kv, H_kv, D)))
+    if out is None:
+        out = torch.empty_like(q)
+        _on_stream([out], stream)
+    else:
+        _check_out("out", out, (B, S_q, H, D), torch.bfloat16, q.device)
+    st = lib.attn_fwd_bf16_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv, H, H_kv, D,
+                              float(scale), int(window[0]), int(window[1]), _stream_handle(stream))
+    _status(lib, "attn_fwd_bf16_ex", st)
     return out
 
 
@@ -315,6 +343,41 @@ def sage_attn_fwd(prepared, S, H, scale, out=None, stream=None):
                            float(scale), _stream_handle(stream))
     _status(lib, "sage_attn_fwd", st)
     return out
+
+
+def sage_attn_fwd_ex(prepared, S_q, S_kv, H, H_kv, scale, window=(-1, -1), out=None, stream=None):
+    """The Sage forward on tensors from sage_prepare_ex, with the shapes and key
+    window of attn_fwd_bf16_ex; output [B, S_q, H, 128] BF16."""
+    import torch
+    lib = load()
+    if len(prepared) < 6:
+        raise ValueError("expected the tensors returned by sage_prepare_ex")
+    prepared = tuple(prepared[:6])
+    q_i8 = prepared[0]
+    if not isinstance(q_i8, torch.Tensor) or q_i8.dim() != 4 or q_i8.device.type != "cuda":
+        raise ValueError("prepared tensors must be the GPU tensors returned by sage_prepare_ex")
+    B, D = int(q_i8.shape[0]), int(q_i8.shape[3])
+    for t, (name, shape, dt) in zip(prepared, _prepared_specs(B, int(S_q), int(H), D, int(S_kv), int(H_kv))):
+        _check_out(name, t, shape, dt, q_i8.device)
+    if out is None:
+        out = torch.empty((B, S_q, H, D), dtype=torch.bfloat16, device=q_i8.device)
+        _on_stream([out], stream)
+    else:
+        _check_out("out", out, (B, S_q, H, D), torch.bfloat16, q_i8.device)
+    st = lib.sage_attn_fwd_ex(*[_ptr(t) for t in prepared], _ptr(out), B, int(S_q), int(S_kv), int(H),
+                              int(H_kv), D, float(scale), int(window[0]), int(window[1]),
+                              _stream_handle(stream))
+    _status(lib, "sage_attn_fwd_ex", st)
+    return out
+
+
+def sage_attention_ex(q, k, v, scale, window=(-1, -1), smooth_k=False, stream=None, **xform):
+    """sage_prepare_ex followed by sage_attn_fwd_ex (xform: the transform arguments of
+    sage_prepare_ex)."""
+    _, S_q, H, _ = _dims(q)
+    _, S_kv, H_kv, _ = _dims(k)
+    prepared = sage_prepare_ex(q, k, v, scale, smooth_k=smooth_k, stream=stream, **xform)
+    return sage_attn_fwd_ex(prepared, S_q, S_kv, H, H_kv, scale, window, stream=stream)
 
 
 def sage_attention(q, k, v, scale, stream=None):

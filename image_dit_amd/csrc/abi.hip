@@ -100,18 +100,28 @@ size_t ditattn_sage_workspace_size(int B, int S_kv, int H_kv) {
   return ditattn::sage_workspace_bytes(B, S_kv, H_kv);
 }
 
-int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, int S, int H,
-                  int D, float scale, hipStream_t stream) {
-  int st = check_shape(DITATTN_ENTRY_ATTN_FWD_BF16, B, S, H, D, scale);
+int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o, int B, int S_q,
+                     int S_kv, int H, int H_kv, int D, float scale, int window_left,
+                     int window_right, hipStream_t stream) {
+  int st = check_sizes(B, S_q, S_kv, H, H_kv, D, scale);
   if (st != DITATTN_OK) return st;
+  if (window_left < -1 || window_right < -1) return DITATTN_EINVAL;
   if (!q || !k || !v || !o) return DITATTN_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return DITATTN_EALIGN;
-  const int64_t bytes = static_cast<int64_t>(B) * S * H * 256;
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+  const int64_t q_bytes = static_cast<int64_t>(B) * S_q * H * 256;
+  const int64_t kv_bytes = static_cast<int64_t>(B) * S_kv * H_kv * 256;
+  if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) ||
+      overlaps(o, q_bytes, v, kv_bytes))
     return DITATTN_EINVAL;
-  if (ditattn::launch_attn_fwd_bf16(q, k, v, o, B, S, H, log2e_scale(scale), stream) != hipSuccess)
-    return DITATTN_EHIP;
+  ditattn::Bf16Args a{q, k, v, o, B, S_q, S_kv, H, H_kv, log2e_scale(scale), window_left,
+                      window_right, 0, 0, 0};
+  if (ditattn::launch_attn_fwd_bf16(a, stream) != hipSuccess) return DITATTN_EHIP;
   return DITATTN_OK;
+}
+
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, int S, int H,
+                  int D, float scale, hipStream_t stream) {
+  return attn_fwd_bf16_ex(q, k, v, o, B, S, S, H, H, D, scale, -1, -1, stream);
 }
 
 int sage_prepare_ex(const void* q, const void* k, const void* v, int8_t* q_i8, float* q_scale,
@@ -190,30 +200,39 @@ int qk_norm_rope_bf16(const void* x, void* out, int B, int S, int H, int D, cons
   return DITATTN_OK;
 }
 
-int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                  const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
-                  int B, int S, int H, int D, float scale, hipStream_t stream) {
-  int st = check_shape(DITATTN_ENTRY_SAGE_ATTN_FWD, B, S, H, D, scale);
+int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                     const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
+                     int B, int S_q, int S_kv, int H, int H_kv, int D, float scale,
+                     int window_left, int window_right, hipStream_t stream) {
+  int st = check_sizes(B, S_q, S_kv, H, H_kv, D, scale);
   if (st != DITATTN_OK) return st;
+  if (window_left < -1 || window_right < -1) return DITATTN_EINVAL;
+  // the kernel addresses a V^T tile row as a 32-bit byte offset c * S_kv_pad, c < 128
+  if (S_kv > DITATTN_MAX_SEQ_SAGE) return DITATTN_EOVERFLOW;
   const void* ptrs[7] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o};
   for (const void* p : ptrs)
     if (!p) return DITATTN_EINVAL;
   for (const void* p : ptrs)
     if (misaligned(p)) return DITATTN_EALIGN;
-  const int64_t bh = static_cast<int64_t>(B) * H;
-  const int64_t s_pad = padded(S);
-  const int64_t code_bytes = bh * s_pad * 128;
-  const int64_t qk_scale_bytes = bh * (s_pad / 32) * 4;
-  const int64_t v_scale_bytes = bh * 128 * 4;
+  const int64_t sqp = padded(S_q), skp = padded(S_kv);
+  const int64_t bhq = static_cast<int64_t>(B) * H, bhk = static_cast<int64_t>(B) * H_kv;
   const void* ins[6] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale};
-  const int64_t in_bytes[6] = {code_bytes, qk_scale_bytes, code_bytes, qk_scale_bytes, code_bytes,
-                               v_scale_bytes};
+  const int64_t in_bytes[6] = {bhq * sqp * 128, bhq * (sqp / 32) * 4, bhk * skp * 128,
+                               bhk * (skp / 32) * 4, bhk * skp * 128, bhk * 128 * 4};
   for (int i = 0; i < 6; ++i)
-    if (overlaps(o, bh * S * 256, ins[i], in_bytes[i])) return DITATTN_EINVAL;
-  if (ditattn::launch_sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S, H,
-                                    static_cast<int>(s_pad), stream) != hipSuccess)
-    return DITATTN_EHIP;
+    if (overlaps(o, bhq * S_q * 256, ins[i], in_bytes[i])) return DITATTN_EINVAL;
+  ditattn::SageArgs a{q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S_q, S_kv, H, H_kv,
+                      static_cast<int>(sqp), static_cast<int>(skp), window_left, window_right,
+                      0, 0, 0};
+  if (ditattn::launch_sage_attn_fwd(a, stream) != hipSuccess) return DITATTN_EHIP;
   return DITATTN_OK;
+}
+
+int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                  const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
+                  int B, int S, int H, int D, float scale, hipStream_t stream) {
+  return sage_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S, S, H, H, D, scale,
+                          -1, -1, stream);
 }
 
 }  // extern "C"

@@ -64,27 +64,43 @@ constexpr int TILE_BYTES = BK * 256;
 constexpr int K_STAGE0 = 0;
 constexpr int V_STAGE0 = 2 * TILE_BYTES;
 
+// First and last key query row i sees (an empty range when hi < lo): lo = i + off - wl
+// (wl >= 0), hi = i + off + wr (wr >= 0), off = S_kv - S_q, clamped to the keys, in 64 bits.
+__device__ __forceinline__ int key_lo(const Bf16Args& a, int i) {
+  if (a.wl < 0) return 0;
+  const int64_t lo = (int64_t)i + a.S_kv - a.S_q - a.wl;
+  return (int)(lo < 0 ? 0 : (lo > a.S_kv ? a.S_kv : lo));
+}
+__device__ __forceinline__ int key_hi(const Bf16Args& a, int i) {
+  if (a.wr < 0) return a.S_kv - 1;
+  const int64_t hi = (int64_t)i + a.S_kv - a.S_q + a.wr;
+  return (int)(hi < -1 ? -1 : (hi > a.S_kv - 1 ? a.S_kv - 1 : hi));
+}
+
 __global__ void __launch_bounds__(NW * 64, DITATTN_BF16_OCC)
-attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                     const __bf16* __restrict__ v, __bf16* __restrict__ o, int S, int H, float c,
-                     int num_qt, int n_tiles) {
+attn_fwd_bf16_kernel(Bf16Args a) {
   constexpr int BQ = NW * 32;
   __shared__ __attribute__((aligned(16))) char lds[4 * TILE_BYTES];  // K stage 0, 1, V stage 0, 1
 
-  const int L = xcd_remap(blockIdx.x, n_tiles);
-  const int bh = L / num_qt;
-  const int qt = L - bh * num_qt;
-  const int b = bh / H, h = bh - b * H;
+  const int L = xcd_remap(blockIdx.x, a.n_tiles);
+  const int bh = L / a.num_qt;
+  int qt = L - bh * a.num_qt;
+  if (a.reverse) qt = a.num_qt - 1 - qt;  // longest key ranges first (causal)
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int hk = h / (a.H / a.H_kv);  // key/value head of this query head
+  const float c = a.c;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, hl = l >> 5, ln = l & 31;
-  const int64_t tok = (int64_t)H * kHeadDim;  // elements between consecutive tokens
-  const uint32_t tok_bytes = (uint32_t)(tok * 2);
-  const int64_t base = ((int64_t)b * S * H + h) * kHeadDim;
-  const __bf16* qbh = q + base;
-  const char* kbh = (const char*)(k + base);
-  const char* vbh = (const char*)(v + base);
-  __bf16* obh = o + base;
+  const int64_t tok = (int64_t)a.H * kHeadDim;       // elements between consecutive Q/O tokens
+  const int64_t tok_kv = (int64_t)a.H_kv * kHeadDim;  // ... and K/V tokens
+  const uint32_t tok_bytes = (uint32_t)(tok_kv * 2);
+  const int64_t base = ((int64_t)b * a.S_q * a.H + h) * kHeadDim;
+  const int64_t base_kv = ((int64_t)b * a.S_kv * a.H_kv + hk) * kHeadDim;
+  const __bf16* qbh = (const __bf16*)a.q + base;
+  const char* kbh = (const char*)((const __bf16*)a.k + base_kv);
+  const char* vbh = (const char*)((const __bf16*)a.v + base_kv);
+  __bf16* obh = (__bf16*)a.o + base;
 
   // Q^T operand, resident for the whole key loop: Q[q0 + ln][16 ks + 8 hl + 0..7].
   const int q0 = qt * BQ + wave * 32;
@@ -92,9 +108,20 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   bf16x8 qf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    if (qi < S) qf[ks] = *(const bf16x8*)(qbh + qi * tok + 16 * ks + 8 * hl);
+    if (qi < a.S_q) qf[ks] = *(const bf16x8*)(qbh + qi * tok + 16 * ks + 8 * hl);
     else qf[ks] = bf16x8{};
   }
+
+  // ---- key range: the workgroup visits the tiles holding a key one of its rows < S_q sees;
+  // a tile needs no mask when every key of it is visible to every row of the workgroup.
+  const int i_first = qt * BQ, i_last = min(qt * BQ + BQ - 1, a.S_q - 1);
+  const int lo_i = key_lo(a, qi), hi_i = key_hi(a, qi);
+  const int lo_last = key_lo(a, i_last), hi_first = key_hi(a, i_first);
+  const int hi_last = key_hi(a, i_last);
+  const int t0 = key_lo(a, i_first) / BK;
+  const int t1 = hi_last >= 0 ? hi_last / BK + 1 : 0;
+  const int n = t1 - t0;  // tiles this workgroup visits (uniform)
+  auto masked_tile = [&](int t) { return t * BK < lo_last || t * BK + BK - 1 > hi_first; };
 
   f32x16 acc[4];  // O^T: channels 32 dt + (accumulator row), this lane's query
   float m = -INFINITY, lsum = 0.0f;
@@ -114,18 +141,18 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // Copy key tile t of K (is_v false) or V (is_v true) into the LDS stage at byte
   // offset dst.  In the ragged last tile, rows past the end repeat the last real
   // key: finite data whose scores are masked to -inf (so P = 0 against it).
-  const int n_kt = (S + BK - 1) / BK;
-  const bool ragged = (S % BK) != 0;
+  const int n_kt = (a.S_kv + BK - 1) / BK;
+  const bool ragged = (a.S_kv % BK) != 0;
   auto issue = [&](const char* src, int t, int dst, bool is_v) {
     const int j0 = t * BK;
-    const char* st = src + (int64_t)j0 * tok * 2;
+    const char* st = src + (int64_t)j0 * tok_kv * 2;
     const bool clamp = ragged && t == n_kt - 1;
 #pragma unroll
     for (int n = 0; n < NCP; ++n) {
       uint32_t off = is_v ? voff[n] : koff[n];
       if (clamp) {
         const int r = RPW * wave + 4 * n + (l >> 4);
-        const int rr = (j0 + r >= S) ? S - 1 - j0 : r;
+        const int rr = (j0 + r >= a.S_kv) ? a.S_kv - 1 - j0 : r;
         off = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ (is_v ? (r & 3) << 2 : r & 15));
       }
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(st + off),
@@ -243,19 +270,23 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       for (int dt = 0; dt < 4; ++dt) pin(acc[dt]);
     }
   };
-  // softmax of the scores of tile q (in sc): mask the ragged end, raise the running
-  // max lazily (rescaling acc and l, whose last update is complete), P -> BF16.
-  auto softmax = [&](int q) {
-    if (ragged && q == n_kt - 1) {
-      // keys 32 tt + 8 (r / 4) + 4 hl + r % 4 of the tile are real below lim + 4 hl; the
-      // opaque move keeps the 32 compares here instead of hoisted out of the key loop
-      int lim = S - q * BK - 4 * hl;
-      asm volatile("" : "+v"(lim));
+  // softmax of the scores of tile t (in sc): mask the keys this lane's query does not
+  // see (tiles crossing a mask boundary only), raise the running max lazily (rescaling
+  // acc and l, whose last update is complete), P -> BF16.
+  auto softmax = [&](int t) {
+    if (masked_tile(t)) {
+      // key t * BK + 32 tt + 8 (r / 4) + 4 hl + r % 4 is visible for offsets
+      // 32 tt + 8 (r / 4) + r % 4 in [elo, ehi]; the opaque moves keep the compares here
+      // instead of hoisted out of the key loop
+      int elo = lo_i - t * BK - 4 * hl, ehi = hi_i - t * BK - 4 * hl;
+      asm volatile("" : "+v"(elo), "+v"(ehi));
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * tt + 8 * (r >> 2) + (r & 3) >= lim) sc[tt][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int e = 32 * tt + 8 * (r >> 2) + (r & 3);
+          if (e < elo || e > ehi) sc[tt][r] = -INFINITY;
+        }
     }
     float mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
@@ -263,13 +294,13 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     mx = half_pair_max(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazyThresh) != 0) {
       const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
+      const float alpha = m_new == m ? 1.0f : fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
     }
-    const float mneg = -m;
+    const float mneg = m == -INFINITY ? 0.0f : -m;  // rows with no visible key yet
     float p[32];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -301,9 +332,9 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // were last read in M(q-1), which both groups finished by barrier 2q, and their
   // first readers (M(q+1) of group A) start at barrier 2q+2.
   const bool grp_a = wave < NW / 2;
-  auto copy = [&](int q) {  // K(q+1) and V(q), where they exist
-    if (q + 1 < n_kt) issue(kbh, q + 1, K_STAGE0 + ((q + 1) & 1) * TILE_BYTES, false);
-    if (q < n_kt) issue(vbh, q, V_STAGE0 + (q & 1) * TILE_BYTES, true);
+  auto copy = [&](int q) {  // K(q+1) and V(q) (local tile indices), where they exist
+    if (q + 1 < n) issue(kbh, t0 + q + 1, K_STAGE0 + ((q + 1) & 1) * TILE_BYTES, false);
+    if (q < n) issue(vbh, t0 + q, V_STAGE0 + (q & 1) * TILE_BYTES, true);
   };
   auto copies_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   // s_barrier without the release fence of __syncthreads(), which would also wait
@@ -313,7 +344,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using I1 = std::integral_constant<int, 1>;
   using T = std::true_type;
   using F = std::false_type;
-  // one period p (1 <= p <= n_kt - 1) with compile-time K stage par = p & 1
+  // one period p (1 <= p <= n - 1) with compile-time K stage par = p & 1
   auto period = [&](auto par_c, int p) {
     constexpr int par = decltype(par_c)::value;
     using KS = std::integral_constant<int, par>;
@@ -323,12 +354,13 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (!grp_a) copies_landed();
     barrier();
     if (!grp_a) copy(p + 1);  // window 2p+2 .. 2p+4
-    softmax(p);
+    softmax(t0 + p);
     if (grp_a) copies_landed();
     barrier();
   };
 
-  issue(kbh, 0, K_STAGE0, false);
+  if (n > 0) {  // uniform: every wave of the workgroup takes the same path
+  issue(kbh, t0, K_STAGE0, false);
   copies_landed();
   barrier();  // barrier 0
   if (!grp_a) {
@@ -341,27 +373,29 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (!grp_a) copies_landed();
   barrier();
   if (!grp_a) copy(1);
-  softmax(0);
+  softmax(t0);
   if (grp_a) copies_landed();
   barrier();
   int p = 1;
-  for (; p + 1 < n_kt; p += 2) {  // two periods per trip: stage offsets are immediates
+  for (; p + 1 < n; p += 2) {  // two periods per trip: stage offsets are immediates
     period(I1{}, p);
     period(I0{}, p + 1);
   }
-  if (p < n_kt) {  // p odd
+  if (p < n) {  // p odd
     period(I1{}, p);
     ++p;
   }
-  // M(n_kt): P V of the last tile only
+  // M(n): P V of the last tile only
   if (p & 1) mphase(I0{}, I0{}, T{}, F{});
   else mphase(I1{}, I0{}, T{}, F{});
   if (grp_a) barrier();  // matches group B's leading barrier
+  }
 
-  // ---- epilogue: O = acc / l, BF16, rows < S
+  // ---- epilogue: O = acc / l, BF16, rows < S_q (0 for a row with no visible key)
   mfma_drain(acc[0], acc[1], acc[2], acc[3]);
-  const float inv = 1.0f / half_pair_sum(lsum);
-  if (qi < S) {
+  const float lt = half_pair_sum(lsum);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (qi < a.S_q) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -380,13 +414,12 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // Query rows per workgroup of the launched configuration.
 constexpr int kBf16BQ = bf16attn::NW * 32;
 
-hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B,
-                                int S, int H, float c, hipStream_t stream) {
-  const int num_qt = (S + kBf16BQ - 1) / kBf16BQ;
-  const int n_tiles = B * H * num_qt;
-  return launch(bf16attn::attn_fwd_bf16_kernel, dim3(n_tiles), dim3(bf16attn::NW * 64), stream,
-                (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, S, H, c, num_qt,
-                n_tiles);
+hipError_t launch_attn_fwd_bf16(const Bf16Args& a0, hipStream_t stream) {
+  Bf16Args a = a0;
+  a.num_qt = (a.S_q + kBf16BQ - 1) / kBf16BQ;
+  a.n_tiles = a.B * a.H * a.num_qt;
+  a.reverse = a.wr >= 0 ? 1 : 0;  // a key range that ends at the query: later tiles see more keys
+  return launch(bf16attn::attn_fwd_bf16_kernel, dim3(a.n_tiles), dim3(bf16attn::NW * 64), stream, a);
 }
 
 }  // namespace ditattn

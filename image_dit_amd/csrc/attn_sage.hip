@@ -1,32 +1,48 @@
 // attn_sage.hip -- Sage attention forward for gfx950 on tensors written by
-// sage_prepare: Q K^T on INT8 MFMA, P V on FP8 (OCP e4m3) MFMA, FP32
-// accumulation, online softmax in base 2, BF16 output.
+// sage_prepare / sage_prepare_ex: Q K^T on INT8 MFMA, P V on FP8 (OCP e4m3)
+// MFMA, FP32 accumulation, online softmax in base 2, BF16 output.
 //
 // Operation: "gfx1201_sage_prepare / gfx1201_sage_attention" (aiter PR 6390),
 // second commit and "Technical Details": the kernel alone on prepared tensors,
-// non-causal, head dim 128.  Online softmax as in "Kernel acceleration:
-// attention, compilation and fusion", section "Attention: from O(N^2) memory
-// to blocks".
+// head dim 128.  Online softmax as in "Kernel acceleration: attention,
+// compilation and fusion", section "Attention: from O(N^2) memory to blocks".
+// Beyond the page's non-causal self-attention: S_q != S_kv (cross-attention),
+// H a multiple of H_kv (grouped-query heads) and an optional key window per
+// query (causal and sliding-window masks), as listed in the "Features" table of
+// the "RDNAttention" README.
 //
 // gfx950 mapping
-//   * Workgroup = 4 waves x 32 query rows (BQ = 128) of one (b, h); XCD-aware
-//     tile order as in the BF16 kernel; two workgroups per CU.  Key tiles of
-//     BK = 64, double-buffered, copied global -> LDS directly.
-//   * S^T = K Q^T on v_mfma_i32_32x32x32_i8 (exact int32; |acc| <= 128 * 127^2
-//     < 2^24 so the conversion to fp32 is exact).  Q codes stay in registers.
-//     Scores in log2 units: x = acc * q_scale[query block] * k_scale[key block].
-//   * Key rows are fed to the A operand in an order that gives every half-wave
-//     32 consecutive keys of the tile (one 32-row K block, hence one k_scale):
-//     P's FP8 B operand of a lane is then 32 consecutive keys, and the matching
-//     V^T operand is two 16-byte LDS reads.
-//   * P V on v_mfma_scale_f32_32x32x64_f8f6f4 (both operands e4m3, unit block
-//     scales): A = V^T tile (channels x 64 keys) in LDS, B = P from registers.
-//   * P is stored as p * 2^8 in e4m3: exp2(x - m + 8) gives it directly.  The
-//     running max is raised lazily (threshold 0.8 in log2 units), so p <= 2^0.8
-//     and p * 2^8 <= 445.7 < 448; values down to 2^-14 stay normal.  The row
-//     sum l accumulates the same fp32 values, so O = acc * v_scale / l.
-//   * Keys j >= S (zero codes, which would score 0) are masked to -inf in the
-//     last tile only.
+//   * Workgroup = 8 waves x 32 query rows (BQ = 256) of one (b, h), all reading
+//     the same K/V tiles of BK = 64 keys from LDS, copied global -> LDS
+//     directly through a three-stage ring.  XCD-aware tile order.
+//   * S^T = K Q^T on v_mfma_i32_32x32x32_i8 (exact int32: |acc| <= 128 * 127^2
+//     < 2^21).  Q codes stay in registers.  Key rows are fed to the A operand in
+//     an order that gives each half-wave 32 consecutive keys, i.e. one 32-row K
+//     block and one k_scale: a lane's scores are x = acc * s with
+//     s = q_scale * k_scale, already in base-2 units.  The accumulators start
+//     at the bit pattern of 1.5 * 2^23, so an int32 sum read as fp32 is exactly
+//     1.5 * 2^23 + score: the row max is taken on those bit patterns and
+//     p = exp2(score * s - m + 8) is one FMA and one exp2, no conversion.
+//   * P V on v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 operands, unit block
+//     scales): A = V^T tile (channels x 64 keys) from LDS, B = P from registers
+//     (the S^T accumulator of a lane already holds the B operand's keys).
+//   * P is stored as p * 2^8 in e4m3; the running max is raised lazily (only
+//     when a row's tile max exceeds it by more than 0.8 in base-2 units), so
+//     p * 2^8 <= 2^8.8 = 445.7 < 448.  The row sum l comes from one more FP8
+//     MFMA of an all-ones A operand with the same P: the matrix unit has slack
+//     here and the vector unit has none, and numerator and denominator then
+//     use the same rounded P.  O = acc * v_scale / l.
+//   * Two wave groups ping-pong on each SIMD (waves w and w + 4 share one):
+//     one group's matrix phase (P V of the previous tile, K Q^T of this one)
+//     runs under the other group's softmax.  The softmax is the longer phase:
+//     a single wave issues at most one vector instruction every few cycles, so
+//     the phase is bound by that issue rate, not by the vector unit's width.
+//   * Masks: keys j >= S_kv (zero codes, which would score 0) and keys outside
+//     a query's window get p = 0.  Only tiles that cross a mask boundary for
+//     some row of the workgroup take the masked path; a row with no visible
+//     key writes zeros.
+#include <stdint.h>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -35,213 +51,344 @@
 namespace ditattn {
 namespace sageattn {
 
-#ifndef DITATTN_SAGE_OCC
-#define DITATTN_SAGE_OCC 2  // workgroups per CU the register budget is sized for
-#endif
-
 constexpr int BK = 64;
-constexpr int NW = 4;
+constexpr int NW = 8;
 constexpr int BQ = NW * 32;
 constexpr float kPScaleLog2 = 8.0f;  // P is stored as p * 2^8
 // The running max is raised only when a row's tile max exceeds it by more than
-// this (log2 units).  P then stays <= 2^0.8, so p * 2^8 <= 445.7 still fits
-// e4m3 (max 448).
+// this (base-2 units).  P then stays <= 2^0.8, so p * 2^8 <= 445.7 fits e4m3.
 constexpr float kLazyThresh = 0.8f;
+constexpr float kSeed = 12582912.0f;  // 1.5 * 2^23, the fp32 value of the accumulator seed 0x4B400000
 
 // LDS tiles (bytes):  K: 64 key rows x 128 B, 16-B chunk c of row r stored at c ^ ((r >> 1) & 7).
 //                     V^T: 128 channel rows x 64 B, chunk c of row r at c ^ ((r >> 2) & 3).
 constexpr int KT_BYTES = BK * 128;
 constexpr int VT_BYTES = 128 * BK;
-constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
+constexpr int NSTAGE = 3;  // copy ring depth
+constexpr int K_STAGE0 = 0;
+constexpr int V_STAGE0 = NSTAGE * KT_BYTES;
+constexpr int KS_STAGE0 = NSTAGE * (KT_BYTES + VT_BYTES);  // the tile's two k_scale values, 16 B per stage
 
 // Accumulator row m of sub-tile tt holds key 32 * ((m >> 2) & 1) + 16 tt + 4 (m >> 3) + (m & 3)
 // of the 64-key tile.  Then register r of a lane in half hl holds key 32 hl + 16 tt + r: P's
 // 32 FP8 bytes of a lane are 32 consecutive keys and V^T is read with two 16-byte loads.
 __device__ __forceinline__ int key_of_row(int m, int tt) { return 32 * ((m >> 2) & 1) + 16 * tt + 4 * (m >> 3) + (m & 3); }
 
-__global__ void __launch_bounds__(NW * 64, DITATTN_SAGE_OCC)
-sage_attn_fwd_kernel(const int8_t* __restrict__ q_i8, const float* __restrict__ q_scale,
-                     const int8_t* __restrict__ k_i8, const float* __restrict__ k_scale,
-                     const uint8_t* __restrict__ v_fp8, const float* __restrict__ v_scale,
-                     __bf16* __restrict__ o, int S, int H, int S_pad, int num_qt, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE_BYTES];  // 32 KB
+// First and last key query row i sees (an empty range when hi < lo).
+__device__ __forceinline__ int key_lo(const SageArgs& a, int i) {
+  if (a.wl < 0) return 0;
+  const int64_t lo = (int64_t)i + a.S_kv - a.S_q - a.wl;
+  return (int)(lo < 0 ? 0 : (lo > a.S_kv ? a.S_kv : lo));
+}
+__device__ __forceinline__ int key_hi(const SageArgs& a, int i) {
+  if (a.wr < 0) return a.S_kv - 1;
+  const int64_t hi = (int64_t)i + a.S_kv - a.S_q + a.wr;
+  return (int)(hi < -1 ? -1 : (hi > a.S_kv - 1 ? a.S_kv - 1 : hi));
+}
 
-  const int L = xcd_remap(blockIdx.x, n_tiles);
-  const int bh = L / num_qt;
-  const int qt = L - bh * num_qt;
-  const int b = bh / H, h = bh - b * H;
+__global__ void __launch_bounds__(NW * 64, 1)
+sage_attn_fwd_kernel(SageArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * (KT_BYTES + VT_BYTES) + NSTAGE * 16];  // 48 KB
+
+  int L = xcd_remap(blockIdx.x, a.n_tiles);
+  const int bh = L / a.num_qt;
+  int qt = L - bh * a.num_qt;
+  if (a.reverse) qt = a.num_qt - 1 - qt;  // longest key ranges first (causal)
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int bhk = b * a.H_kv + h / (a.H / a.H_kv);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, hl = l >> 5, ln = l & 31;
-  const int nblk = S_pad / 32;
+  const int nblk_q = a.S_q_pad / 32, nblk_k = a.S_kv_pad / 32;
 
-  const int8_t* qbh = q_i8 + (int64_t)bh * S_pad * kHeadDim;
-  const char* kbh = (const char*)(k_i8 + (int64_t)bh * S_pad * kHeadDim);
-  const char* vbh = (const char*)(v_fp8 + (int64_t)bh * kHeadDim * S_pad);
-  const float* ksc = k_scale + (int64_t)bh * nblk;
+  const int8_t* qbh = a.q_i8 + (int64_t)bh * a.S_q_pad * kHeadDim;
+  const char* kbh = (const char*)(a.k_i8 + (int64_t)bhk * a.S_kv_pad * kHeadDim);
+  const char* vbh = (const char*)(a.v_fp8 + (int64_t)bhk * kHeadDim * a.S_kv_pad);
+  const float* ksc = a.k_scale + (int64_t)bhk * nblk_k;
 
-  // Q codes (B operand), resident: Q[q0 + ln][32 ks + 16 hl + 0..15].  Rows < S_pad always.
+  // Q codes (B operand), resident: Q[q0 + ln][32 ks + 16 hl + 0..15].  Rows < S_q_pad always.
   const int q0 = qt * BQ + wave * 32;
+  const int qi = q0 + ln;  // this lane's query row
   i32x4 qf[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const i32x4*)(qbh + (int64_t)(q0 + ln) * kHeadDim + 32 * ks + 16 * hl);
-  const float sq = q_scale[(int64_t)bh * nblk + q0 / 32];
+  for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const i32x4*)(qbh + (int64_t)qi * kHeadDim + 32 * ks + 16 * hl);
+  const float sq = a.q_scale[(int64_t)bh * nblk_q + q0 / 32];
 
-  f32x16 acc[4];
+  // ---- key range.  Query i sees keys j with lo(i) <= j <= hi(i): lo = i + off - wl (wl >= 0),
+  // hi = i + off + wr (wr >= 0), off = S_kv - S_q, both clamped to [0, S_kv - 1] (computed in
+  // 64 bits).  The workgroup visits the tiles holding a key that one of its rows < S_q sees.
+  const int i_first = qt * BQ, i_last = min(qt * BQ + BQ - 1, a.S_q - 1);
+  const int lo_i = key_lo(a, qi), hi_i = key_hi(a, qi);
+  const int lo_first = key_lo(a, i_first), lo_last = key_lo(a, i_last);
+  const int hi_first = key_hi(a, i_first), hi_last = key_hi(a, i_last);
+  const int t0 = lo_first / BK;
+  const int t1 = hi_last >= 0 ? hi_last / BK + 1 : 0;
+  const int n = t1 - t0;  // tiles this workgroup visits (uniform)
+  // a tile needs no mask when every key of it is visible to every row of the workgroup
+  auto masked_tile = [&](int t) __attribute__((always_inline)) { return t * BK < lo_last || t * BK + BK - 1 > hi_first; };
+
+  f32x16 acc[4];  // O^T: channels 32 dt + (accumulator row), this lane's query
+  f32x16 lacc;    // row sums (every accumulator row holds this lane's query's l)
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  float m = -INFINITY, lsum = 0.0f;
+  lacc = f32x16{};
+  float m = -INFINITY;
   const int unit_scale = unit_e8m0_scale();
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
-  // ---- global -> LDS (direct); every lane fetches the chunk that lands in its LDS slot.
-  // K: instruction n of wave w fills LDS rows 8 (2 w + n) .. + 7 (1 KB), lane -> row + l / 8, slot l % 8.
-  // V^T: instruction n of wave w fills channel rows 16 (2 w + n) .. + 15, lane -> row + l / 4, slot l % 4.
-  uint32_t kgo[2], vgo[2];
+  if (n > 0) {
+    // ---- global -> LDS (direct); every lane fetches the chunk that lands in its LDS slot.
+    // K: wave w fills rows 8 w .. 8 w + 7 (1 KB), lane -> row 8 w + l / 8, slot l % 8.
+    // V^T: wave w fills channel rows 16 w .. 16 w + 15, lane -> row 16 w + l / 4, slot l % 4.
+    // Tiles never reach past S_kv_pad, where the codes are zero.
+    const int kr = 8 * wave + (l >> 3), vr = 16 * wave + (l >> 2);
+    const uint32_t kgo = kr * 128 + 16 * ((l & 7) ^ ((kr >> 1) & 7));
+    const uint32_t vgo = vr * a.S_kv_pad + 16 * ((l & 3) ^ ((vr >> 2) & 3));
+    // The k_scale values of the tile's two 32-key blocks travel with its K rows (lanes 0, 1 of
+    // wave 0), so the softmax reads them from LDS instead of waiting on a global load.
+    auto issue_k = [&](int t, int stage) __attribute__((always_inline)) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbh + (int64_t)t * BK * kHeadDim + kgo),
+                                       (DITATTN_LDS void*)(lds + K_STAGE0 + stage * KT_BYTES + wave * 1024), 16, 0, 0);
+      if (wave == 0 && l < 2)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ksc + 2 * t + l),
+                                         (DITATTN_LDS void*)(lds + KS_STAGE0 + stage * 16), 4, 0, 0);
+    };
+    auto issue_v = [&](int t, int stage) __attribute__((always_inline)) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbh + t * BK + vgo),
+                                       (DITATTN_LDS void*)(lds + V_STAGE0 + stage * VT_BYTES + wave * 1024), 16, 0, 0);
+    };
+
+    // ---- per-lane LDS read offsets
+    // K (A operand): row key_of_row(ln, tt) (tt = 1 adds 16 rows, same swizzle), logical chunk 2 ks + hl.
+    uint32_t kofs[4];
+    {
+      const int row = key_of_row(ln, 0);
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int kr = 8 * (2 * wave + n) + (l >> 3), kc = (l & 7) ^ ((kr >> 1) & 7);
-    kgo[n] = kr * 128 + 16 * kc;
-    const int vr = 16 * (2 * wave + n) + (l >> 2), vc = (l & 3) ^ ((vr >> 2) & 3);
-    vgo[n] = vr * S_pad + 16 * vc;
-  }
-  auto issue = [&](int t, int stage) {
-    const int j0 = t * BK;
-    const char* kt = kbh + (int64_t)j0 * kHeadDim;
-    const char* vt = vbh + j0;
-    char* dst = lds + stage * STAGE_BYTES;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + kgo[n]),
-                                       (DITATTN_LDS void*)(dst + (2 * wave + n) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + vgo[n]),
-                                       (DITATTN_LDS void*)(dst + KT_BYTES + (2 * wave + n) * 1024), 16, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) kofs[ks] = row * 128 + 16 * ((2 * ks + hl) ^ ((row >> 1) & 7));
     }
-  };
-
-  // ---- per-lane LDS read offsets
-  // K (A operand): row key_of_row(ln, tt) (tt = 1 adds 16 rows, same swizzle), logical chunk 2 ks + hl.
-  uint32_t kofs[4];
-  {
-    const int row = key_of_row(ln, 0);
+    // V^T (A operand of P V): channel row 32 dt + ln (dt adds 32 rows = 2 KB, same swizzle),
+    // keys 32 hl + 0..31 = logical chunks 2 hl, 2 hl + 1.
+    uint32_t vofs[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kofs[ks] = row * 128 + 16 * ((2 * ks + hl) ^ ((row >> 1) & 7));
-  }
-  // V^T (A operand of P V): channel row 32 dt + ln (dt adds 32 rows = 2 KB, same swizzle),
-  // keys 32 hl + 0..31 = logical chunks 2 hl, 2 hl + 1.
-  uint32_t vofs[2];
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2) vofs[c2] = ln * 64 + 16 * ((2 * hl + c2) ^ ((ln >> 2) & 3));
+    for (int c2 = 0; c2 < 2; ++c2) vofs[c2] = ln * 64 + 16 * ((2 * hl + c2) ^ ((ln >> 2) & 3));
 
-  const int n_kt = (S + BK - 1) / BK;
-  const bool ragged = (S % BK) != 0;
-
-  // One key tile from LDS stage `stage` (a constant in the main loop, a runtime
-  // value for the last tile, which always goes through one code path so that
-  // nothing is merged between its last MFMA and the epilogue).
-  auto tile = [&](auto stage_v, auto tail_c, int t) {
-    constexpr bool tail = decltype(tail_c)::value;
-    const int stage = stage_v;
-    const DITATTN_LDS char* kb = (const DITATTN_LDS char*)(lds + stage * STAGE_BYTES);
-    const DITATTN_LDS char* vb = kb + KT_BYTES;
-    const int j0 = t * BK;
-
-    // ---- S^T = K Q^T (int32)
-    i32x16 si[2];
+    // The K Q^T accumulators start at the bit pattern of 1.5 * 2^23 (0x4B400000): with
+    // |score| < 2^21 the int32 sum read as fp32 is then exactly 1.5 * 2^23 + score, so the
+    // scores need no int -> fp32 conversion (see the softmax).
+    i32x16 seed;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      si[tt] = i32x16{};
+    for (int r = 0; r < 16; ++r) seed[r] = 0x4B400000;
+    i32x16 si[2];  // biased int32 scores of the latest tile, one 32-key sub-tile each
+    i32x8 pf;      // P of the latest softmax (e4m3, p * 2^8)
+    float s_tile;  // q_scale * k_scale of the half-wave's 32-key block in that tile
+    // ---- matrix phase: O^T += V^T P^T (and the row sums) for V stage VS (4 + 1 MFMA) and/or
+    // S^T = K Q^T for K stage KS (8 MFMA).
+    auto mphase = [&](auto vs_c, auto ks_c, auto pv_c, auto qk_c) __attribute__((always_inline)) {
+      constexpr int VS = decltype(vs_c)::value, KS = decltype(ks_c)::value;
+      constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
+      const DITATTN_LDS char* kb = (const DITATTN_LDS char*)(lds + K_STAGE0 + KS * KT_BYTES);
+      const DITATTN_LDS char* vb = (const DITATTN_LDS char*)(lds + V_STAGE0 + VS * VT_BYTES);
+      if constexpr (PV) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const i32x4 kf = *(const DITATTN_LDS i32x4*)(kb + kofs[ks] + tt * 16 * 128);
-        si[tt] = mfma_i8_32x32x32(kf, qf[ks], si[tt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          const i32x4 v0 = *(const DITATTN_LDS i32x4*)(vb + vofs[0] + dt * 32 * 64);
+          const i32x4 v1 = *(const DITATTN_LDS i32x4*)(vb + vofs[1] + dt * 32 * 64);
+          const i32x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[dt] = mfma_fp8_32x32x64(va, pf, acc[dt], unit_scale);
+        }
+        lacc = mfma_fp8_32x32x64(ones, pf, lacc, unit_scale);
       }
-    }
-    // a lane's 32 keys (32 hl + 0..31) are exactly one 32-row K block
-    const float sc = sq * ksc[(j0 >> 5) + hl];
-    float x[32];
+      if constexpr (QK) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[16 * tt + r] = (float)si[tt][r] * sc;
-    if constexpr (tail) {
-      if (ragged) {
-#pragma unroll
-        for (int e = 0; e < 32; ++e)
-          if (j0 + 32 * hl + e >= S) x[e] = -INFINITY;
+          for (int ks = 0; ks < 4; ++ks) {
+            const i32x4 kf = *(const DITATTN_LDS i32x4*)(kb + kofs[ks] + tt * 16 * 128);
+            si[tt] = mfma_i8_32x32x32(kf, qf[ks], ks == 0 ? seed : si[tt]);
+          }
+        }
+        // read with the K rows: the stage is refilled one window later, while the
+        // other group may still be in this tile's softmax
+        s_tile = sq * *(const DITATTN_LDS float*)(lds + KS_STAGE0 + KS * 16 + 4 * hl);
+        pin(si[0]);
+        pin(si[1]);
       }
-    }
-    float mx = fmaxf(x[0], x[1]);
+      if constexpr (PV) {
 #pragma unroll
-    for (int e = 2; e < 32; e += 2) mx = max3(mx, x[e], x[e + 1]);
-    mx = half_pair_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m + kLazyThresh) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
-    }
-    const float mneg = kPScaleLog2 - m;
-    // P (B operand, 32 e4m3 bytes): byte e = key 32 hl + e
-    i32x8 pf;
-    float p[32];
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) p[4 * w + u] = fast_exp2(x[4 * w + u] + mneg);
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
-      pf[w] = word;
-    }
-    lsum += tree_sum<32>(p);
+        for (int dt = 0; dt < 4; ++dt) pin(acc[dt]);
+        pin(lacc);
+      }
+    };
 
-    // ---- O^T += V^T P^T
+    // ---- softmax of the scores of tile t (in si): lazily raised running max, P -> e4m3.
+    // One body for every tile (two copies of it make the compiler double-allocate the
+    // accumulators); a tile crossing a mask boundary only takes two small branches: its
+    // hidden scores become INT32_MIN before the row max, and their p become 0 after exp2.
+    auto softmax = [&](int t) __attribute__((always_inline)) {
+      const float s = s_tile;
+      constexpr int kMasked = INT32_MIN;  // no real score gets there: |acc| <= 128 * 127^2
+      const bool masked = masked_tile(t);  // uniform
+      if (masked) {
+        // keys t * BK + 32 hl + e, e = 16 tt + r, visible for e in [elo, ehi]
+        const int elo = lo_i - (t * BK + 32 * hl), ehi = hi_i - (t * BK + 32 * hl);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const i32x4 v0 = *(const DITATTN_LDS i32x4*)(vb + vofs[0] + dt * 32 * 64);
-      const i32x4 v1 = *(const DITATTN_LDS i32x4*)(vb + vofs[1] + dt * 32 * 64);
-      const i32x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[dt] = mfma_fp8_32x32x64(va, pf, acc[dt], unit_scale);
-    }
-  };
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = 16 * tt + r;
+            si[tt][r] = (e < elo || e > ehi) ? kMasked : si[tt][r];
+          }
+      }
+      // row max on the biased int32 patterns (positive floats order like their bits), as a
+      // tree of v_max3_i32 for a short dependency chain
+      int m8[11];
+#pragma unroll
+      for (int j = 0; j < 10; ++j) {
+        const int e = 3 * j;
+        m8[j] = max(max(si[e >> 4][e & 15], si[(e + 1) >> 4][(e + 1) & 15]), si[(e + 2) >> 4][(e + 2) & 15]);
+      }
+      m8[10] = max(si[1][14], si[1][15]);
+      const int mi = max(max(max(max(m8[0], m8[1]), m8[2]), max(max(m8[3], m8[4]), m8[5])),
+                         max(max(max(m8[6], m8[7]), m8[8]), max(m8[9], m8[10])));
+      // s >= 0: scaling keeps the max; a half-wave with every key hidden contributes -inf
+      float mx = mi == kMasked ? -INFINITY : (__int_as_float(mi) - kSeed) * s;
+      mx = half_pair_max(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m + kLazyThresh) != 0) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = m_new == m ? 1.0f : fast_exp2(m - m_new);
+        m = m_new;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+        lacc *= alpha;
+      }
+      const float mneg = m == -INFINITY ? 0.0f : kPScaleLog2 - m;  // rows with no visible key yet
+      // x = score * s - m + 8 as ONE fma on the biased pattern A = 1.5 * 2^23 + score:
+      // A * s + (mneg - 1.5 * 2^23 * s).  The constant's rounding error is below 0.75 s, i.e.
+      // under one unit of the int32 dot product (whose INT8 quantization noise is far larger).
+      const float cst = fmaf(-kSeed, s, mneg);
+      float p[32];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[16 * tt + r] = fast_exp2(fmaf(__int_as_float(si[tt][r]), s, cst));
+      if (masked) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[16 * tt + r] = si[tt][r] == kMasked ? 0.0f : p[16 * tt + r];
+      }
+      // P (B operand, 32 e4m3 bytes): byte e = key 32 hl + e
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
+        pf[w] = word;
+      }
+      // keep the softmax in its phase: without the pin the compiler sinks the
+      // exponentials past the barrier, next to the P V products that consume them
+      asm volatile("" : "+v"(pf));
+    };
+    auto softmax_tile = [&](int t) __attribute__((always_inline)) { softmax(t); };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using Full = std::integral_constant<bool, false>;
-  using Last = std::integral_constant<bool, true>;
-  const int n_main = n_kt - 1;  // tiles before the last one
+    // ---- ping-pong over key tiles t0 .. t1 - 1 (local index p = t - t0), as in the BF16
+    // kernel.  Waves w and w + 4 share a SIMD.  Every wave runs
+    //   M(0) | V(0) | M(1) | V(1) | ... | M(n)
+    // with a barrier after each phase, where M(p) = [P V of tile p-1, K Q^T of tile p] and
+    // V(p) = softmax of tile p; group B (waves 4-7) starts one barrier late, so on each SIMD
+    // one wave's matrix phase overlaps the other's softmax.  Barrier k: group A has finished
+    // phase k-1 of its sequence, group B phase k-2.  K(p+1) and V(p) are copied in the window
+    // between barriers 2p and 2p+2, each group its own rows (issued at the window's start,
+    // awaited at its end): the stages they overwrite (K(p-1), V(p-2)) were last read in
+    // M(p-1), which both groups finished by barrier 2p, and their first readers (M(p+1) of
+    // group A) start at barrier 2p+2.
+    const bool grp_a = wave < NW / 2;
+    // copy(q) = K(q+2) and V(q+1), where they exist, into stages (q+2) % 3 and (q+1) % 3
+    auto copy = [&](int q) __attribute__((always_inline)) {
+      if (q + 2 < n) issue_k(t0 + q + 2, (q + 2) % NSTAGE);
+      if (q + 1 < n) issue_v(t0 + q + 1, (q + 1) % NSTAGE);
+    };
+    // wait until the copies of the previous window have landed; the current window's (one
+    // K and one V instruction per wave, plus a scale load on wave 0) may stay in flight
+    auto prev_landed = [&](int q) __attribute__((always_inline)) {
+      if (q + 2 < n) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    // s_barrier without the release fence of __syncthreads(), which would also wait for the
+    // copies in flight; LDS reads before it have all been consumed.
+    auto barrier = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using T = std::true_type;
+    using F = std::false_type;
+    // ---- ping-pong over key tiles t0 .. t1 - 1 (local index p).  Waves w and w + 4 share a
+    // SIMD.  Every wave runs  M(0) | V(0) | M(1) | V(1) | ... | M(n)  with a barrier after each
+    // phase, M(p) = [P V of tile p-1, K Q^T of tile p], V(p) = softmax of tile p; group B
+    // (waves 4-7) starts one barrier late, so on each SIMD one wave's matrix phase overlaps
+    // the other's softmax.  Barrier k: group A has finished phase k-1, group B phase k-2.
+    // Three-stage copy ring: window q (barriers 2q .. 2q+2) copies K(q+2) and V(q+1), each
+    // group its own rows at the start of its M(q); they must land by barrier 2q+4, where
+    // group A's M(q+2) first reads them, and each group waits for them at the end of its last
+    // phase before that barrier (one full window after the issue).  The stages they refill
+    // held K(q-1) and V(q-2), last read in M(q-1), finished by both groups at barrier 2q.
+    // The k_scale pair of a tile is read in the M phase with its K rows.
+    auto period = [&](auto st_c, int p) __attribute__((always_inline)) {  // 1 <= p <= n - 1, st = p % 3
+      constexpr int st = decltype(st_c)::value;
+      using KS = std::integral_constant<int, st>;
+      using VS = std::integral_constant<int, (st + NSTAGE - 1) % NSTAGE>;
+      copy(p);
+      mphase(VS{}, KS{}, T{}, T{});
+      if (!grp_a) prev_landed(p);
+      barrier();
+      softmax_tile(t0 + p);
+      if (grp_a) prev_landed(p);
+      barrier();
+    };
 
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  int t = 0;
-  for (; t + 1 < n_main; t += 2) {  // two tiles per trip: stage offsets are immediates
-    issue(t + 1, 1);
-    tile(I0{}, Full{}, t);
+    issue_k(t0, 0);
+    if (n > 1) issue_k(t0 + 1, 1);
+    issue_v(t0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue(t + 2, 0);
-    tile(I1{}, Full{}, t + 1);
+    barrier();  // barrier 0
+    if (!grp_a) barrier();  // group B's leading barrier (barrier 1 for group A)
+    // period 0: no P V yet, no window before it to wait for
+    copy(0);
+    mphase(I0{}, I0{}, F{}, T{});
+    barrier();
+    softmax_tile(t0);
+    barrier();
+    int p = 1;
+    for (; p + 2 < n; p += 3) {  // three periods per trip: stage offsets are immediates
+      period(I1{}, p);
+      period(I2{}, p + 1);
+      period(I0{}, p + 2);
+    }
+    if (p < n) {
+      period(I1{}, p);
+      ++p;
+    }
+    if (p < n) {
+      period(I2{}, p);
+      ++p;
+    }
+    // M(n): P V of the last tile (n - 1) from V stage (n - 1) % 3
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    const int vs_last = (n - 1) % NSTAGE;
+    if (vs_last == 0) mphase(I0{}, I0{}, T{}, F{});
+    else if (vs_last == 1) mphase(I1{}, I0{}, T{}, F{});
+    else mphase(I2{}, I0{}, T{}, F{});
+    if (grp_a) barrier();  // matches group B's leading barrier
   }
-  if (t < n_main) {  // one more tile before the last, in stage 0 (t is even)
-    issue(t + 1, 1);
-    tile(I0{}, Full{}, t);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    ++t;
-  }
-  tile(t & 1, Last{}, t);  // the last tile (masked when S is ragged)
 
-  // ---- epilogue: O[i][d] = acc * v_scale[d] / l
+  // ---- epilogue: O[i][d] = acc * v_scale[d] / l (0 for a row with no visible key)
   mfma_drain(acc[0], acc[1], acc[2], acc[3]);
-  const float inv = 1.0f / half_pair_sum(lsum);
-  const int i = q0 + ln;
-  if (i < S) {
-    const float* vsc = v_scale + (int64_t)bh * kHeadDim;
-    __bf16* orow = o + (((int64_t)b * S + i) * H + h) * kHeadDim;
+  mfma_drain(lacc);
+  const float lsum = lacc[0];
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  if (qi < a.S_q) {
+    const float* vsc = a.v_scale + (int64_t)bhk * kHeadDim;
+    __bf16* orow = (__bf16*)a.o + (((int64_t)b * a.S_q + qi) * a.H + h) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -258,14 +405,13 @@ sage_attn_fwd_kernel(const int8_t* __restrict__ q_i8, const float* __restrict__ 
 
 }  // namespace sageattn
 
-hipError_t launch_sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                                const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                                void* o, int B, int S, int H, int S_pad, hipStream_t stream) {
-  const int num_qt = (S + sageattn::BQ - 1) / sageattn::BQ;
-  const int n_tiles = B * H * num_qt;
-  return launch(sageattn::sage_attn_fwd_kernel, dim3(n_tiles), dim3(sageattn::NW * 64), stream,
-                q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, (__bf16*)o, S, H, S_pad, num_qt,
-                n_tiles);
+hipError_t launch_sage_attn_fwd(const SageArgs& a0, hipStream_t stream) {
+  SageArgs a = a0;
+  a.num_qt = (a.S_q + sageattn::BQ - 1) / sageattn::BQ;
+  a.n_tiles = a.B * a.H * a.num_qt;
+  a.reverse = a.wr >= 0 ? 1 : 0;  // a key range that ends at the query: later tiles see more keys
+  return launch(sageattn::sage_attn_fwd_kernel, dim3(a.n_tiles), dim3(sageattn::NW * 64), stream, a);
 }
 
 }  // namespace ditattn
+

@@ -9,9 +9,17 @@
 
 namespace ditattn {
 
-// c = float(double(scale) * log2(e)) is computed once by the caller.
-hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B,
-                                int S, int H, float c, hipStream_t stream);
+// Arguments of the BF16 attention kernel.
+struct Bf16Args {
+  const void *q, *k, *v;  // BF16 [B, S_q, H, 128] and [B, S_kv, H_kv, 128] (k, v)
+  void* o;                // BF16 [B, S_q, H, 128]
+  int B, S_q, S_kv, H, H_kv;
+  float c;                // float(double(scale) * log2(e)), computed once by the caller
+  int wl, wr;             // key window (-1 = unbounded on that side)
+  int num_qt, n_tiles, reverse;  // filled in by the launcher
+};
+
+hipError_t launch_attn_fwd_bf16(const Bf16Args& a, hipStream_t stream);
 
 // Everything sage_prepare / sage_prepare_ex pass to the prepare kernels.
 struct PrepareArgs {
@@ -41,9 +49,21 @@ hipError_t launch_qk_norm_rope(const void* x, void* out, int B, int S, int H, co
                                float eps, const void* cos_t, const void* sin_t, int rope_dim,
                                hipStream_t stream);
 
-hipError_t launch_sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                                const float* k_scale, const uint8_t* v_fp8, const float* v_scale,
-                                void* o, int B, int S, int H, int S_pad, hipStream_t stream);
+// Arguments of the Sage attention kernel (tensors as written by the prepare stage).
+struct SageArgs {
+  const int8_t* q_i8;     // [B, H, S_q_pad, 128]
+  const float* q_scale;   // [B, H, S_q_pad / 32]
+  const int8_t* k_i8;     // [B, H_kv, S_kv_pad, 128]
+  const float* k_scale;   // [B, H_kv, S_kv_pad / 32]
+  const uint8_t* v_fp8;   // [B, H_kv, 128, S_kv_pad]
+  const float* v_scale;   // [B, H_kv, 128]
+  void* o;                // BF16 [B, S_q, H, 128]
+  int B, S_q, S_kv, H, H_kv, S_q_pad, S_kv_pad;
+  int wl, wr;             // key window (-1 = unbounded on that side)
+  int num_qt, n_tiles, reverse;  // filled in by the launcher
+};
+
+hipError_t launch_sage_attn_fwd(const SageArgs& a, hipStream_t stream);
 
 namespace detail {
 template <typename K, typename T, std::size_t... I>

@@ -7,8 +7,8 @@ path and the CPU oracle consume exactly the BF16 bits it produces.
 Workloads stand in for the DiT self-attention shapes the pages list
 ("Kernel acceleration: attention, compilation and fusion", section
 "Attention: from O(N^2) memory to blocks", token-count table: FLUX 1024^2 has
-4608 tokens, FLUX 2048^2 16896, Wan 2.1 720p 76112; 24 x 128 and 40 x 128
-channels) with randn inputs as in the randn benchmark of
+4608 tokens, FLUX 2048^2 16896, Wan 2.1 720p 76112, HunyuanVideo 720p 119056;
+24 x 128 and 40 x 128 channels) with randn inputs as in the randn benchmark of
 "gfx1201_sage_prepare / gfx1201_sage_attention", section "Test Result".
 The K bias of the FLUX-Sage and Wan workloads mimics DiT outlier channels: one
 N(0, std = 2) value per (head, channel), shared by every token and batch.
@@ -48,6 +48,7 @@ WORKLOADS = {
     "flux1024_kbias": Workload("flux1024_kbias", 1, 24, 4608, 1003, k_bias_std=2.0),
     "flux2048": Workload("flux2048", 1, 24, 16896, 1004),
     "wan720p": Workload("wan720p", 1, 40, 76112, 1005, k_bias_std=2.0),
+    "hunyuan720p": Workload("hunyuan720p", 1, 24, 119056, 1006, k_bias_std=2.0),
 }
 
 

@@ -104,6 +104,26 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int B, i
                   int D, float scale, hipStream_t stream);
 
 /*
+ * attn_fwd_bf16_ex -- attn_fwd_bf16 for cross-attention, grouped-query heads and
+ * a key window ("RDNAttention" README, "Features": cross-attention and decode
+ * with seq_len != key_seq_len, GQA/MQA, causal masking, one- or two-sided
+ * sliding window).
+ *   q, o    : BF16 [B, S_q, H, 128];  k, v : BF16 [B, S_kv, H_kv, 128]
+ *   H must be a multiple of H_kv; query head h reads key/value head h / (H / H_kv).
+ *   Query i sees key j when lo(i) <= j <= hi(i), with off = S_kv - S_q (queries
+ *   aligned to the END of the keys, so a decode step S_q = 1 sees every key):
+ *     lo(i) = i + off - window_left   (no lower bound when window_left == -1)
+ *     hi(i) = i + off + window_right  (no upper bound when window_right == -1)
+ *   (-1, -1) is full attention, (-1, 0) causal, (w, 0) a one-sided and (w, w)
+ *   a two-sided sliding window.  Other negative values are DITATTN_EINVAL.
+ *   A query row that sees no key is written as zeros.
+ * attn_fwd_bf16(...) equals attn_fwd_bf16_ex(..., S, S, H, H, ..., -1, -1, ...).
+ */
+int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o, int B, int S_q,
+                     int S_kv, int H, int H_kv, int D, float scale, int window_left,
+                     int window_right, hipStream_t stream);
+
+/*
  * sage_prepare -- quantize BF16 Q, K, V for sage_attn_fwd.  [SAGE] first
  * commit and "Technical Details" (Q/K to INT8 with one FP32 scale per
  * (batch, head, 32-row block), Q carrying scale * log2(e); V to FP8 e4m3
@@ -206,6 +226,19 @@ int qk_norm_rope_bf16(const void* x, void* out, int B, int S, int H, int D, cons
 int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                   const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
                   int B, int S, int H, int D, float scale, hipStream_t stream);
+
+/*
+ * sage_attn_fwd_ex -- sage_attn_fwd on tensors written by sage_prepare_ex, with the
+ * shapes and key window of attn_fwd_bf16_ex (same arguments and meaning):
+ *   q_i8 [B, H, S_q_pad, 128], q_scale [B, H, S_q_pad / 32], k_i8 [B, H_kv, S_kv_pad, 128],
+ *   k_scale [B, H_kv, S_kv_pad / 32], v_fp8 [B, H_kv, 128, S_kv_pad], v_scale [B, H_kv, 128],
+ *   o BF16 [B, S_q, H, 128].  S_kv <= DITATTN_MAX_SEQ_SAGE.
+ * sage_attn_fwd(...) equals sage_attn_fwd_ex(..., S, S, H, H, ..., -1, -1, ...).
+ */
+int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                     const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
+                     int B, int S_q, int S_kv, int H, int H_kv, int D, float scale,
+                     int window_left, int window_right, hipStream_t stream);
 
 #ifdef __cplusplus
 }

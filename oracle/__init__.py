@@ -60,12 +60,14 @@ def _lib():
         lib.oracle_quant_v.argtypes = [u16p, ci, ci, ci, ci, ci, u8p, f32p]
         lib.oracle_quant_qk_mean.argtypes = [u16p, ci, ci, ci, ci, cf, ci, f32p, i8p, f32p]
         lib.oracle_channel_mean.argtypes = [u16p, ci, ci, ci, ci, f32p]
+        lib.oracle_attn_rows_ex.argtypes = [u16p, u16p, u16p, ci, ci, ci, ci, ci, ci, cf, ci, ci,
+                                            i64p, ctypes.c_int64, f64p, ci]
         lib.oracle_f32_to_bf16.argtypes = [cf]
         lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
         lib.oracle_qk_norm_rope.argtypes = [u16p, ci, ci, ci, ci, u16p, cf, u16p, u16p, ci, u16p]
         for name in ("oracle_softmax_row", "oracle_attn_rows", "oracle_attn_blocked",
                      "oracle_quant_qk", "oracle_quant_v", "oracle_qk_norm_rope",
-                     "oracle_quant_qk_mean", "oracle_channel_mean"):
+                     "oracle_quant_qk_mean", "oracle_channel_mean", "oracle_attn_rows_ex"):
             getattr(lib, name).restype = ci
         _LIB = lib
     return _LIB
@@ -134,6 +136,31 @@ def attn_rows(q, k, v, scale, rows=None, nthreads=0):
            "oracle_attn_rows")
     if full:
         return out.reshape(B, S, H, D)
+    return out
+
+
+def attn_rows_ex(q, k, v, scale, window=(-1, -1), rows=None, nthreads=0):
+    """Exact fp64 attention with q [B, S_q, H, D], k and v [B, S_kv, H_kv, D]
+    (query head h reads key/value head h // (H // H_kv)) and a key window
+    (wl, wr): query i sees key j when i + off - wl <= j <= i + off + wr,
+    off = S_kv - S_q, a negative bound meaning none on that side.  A row that
+    sees no key is 0.  rows: n x 3 (b, h, i) or None for every row ([B, S_q, H, D])."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, S_q, H, D = q.shape
+    _, S_kv, H_kv, _ = k.shape
+    full = rows is None
+    if full:
+        b, i, h = np.meshgrid(np.arange(B), np.arange(S_q), np.arange(H), indexing="ij")
+        rows = np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], D), dtype=np.float64)
+    _check(_lib().oracle_attn_rows_ex(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                      _ptr(v, ctypes.c_uint16), B, S_q, S_kv, H, H_kv, D, scale,
+                                      int(window[0]), int(window[1]), _ptr(rows, ctypes.c_int64),
+                                      rows.shape[0], _ptr(out, ctypes.c_double), nthreads),
+           "oracle_attn_rows_ex")
+    if full:
+        return out.reshape(B, S_q, H, D)
     return out
 
 

@@ -38,6 +38,11 @@
  *         V codes [B, H, 128, S_pad], V scales [B, H, 128].  Pad rows, pad
  *         columns and pad blocks are 0.
  *
+ *  1b. Exact attention for cross-attention (S_q != S_kv), grouped-query heads
+ *     (H a multiple of H_kv) and a key window per query ("RDNAttention"
+ *     README, "Features"): oracle_attn_rows_ex, same naive form, with each
+ *     query row restricted to the keys it sees (queries aligned to the end of
+ *     the keys); a row that sees no key is 0 by definition.
  *  3. The optional Q/K row transform of the prepare stage (same page, first
  *     commit and "Technical Details": RMSNorm and rotate-half RoPE with
  *     rope_dim 32/64/96/128, rounded like the eager PyTorch BF16 sequence).
@@ -497,4 +502,75 @@ int oracle_channel_mean(const uint16_t* x, int B, int S, int H, int D, float* me
         mean[((int64_t)b * H + h) * D + d] = (float)(s / (double)S);
       }
   return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 1b. Exact attention with a key window, S_q != S_kv and grouped heads       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * q: BF16 [B, S_q, H, D]; k, v: BF16 [B, S_kv, H_kv, D]; query head h reads
+ * key/value head h / (H / H_kv).  Query i sees key j when lo <= j <= hi with
+ * off = S_kv - S_q, lo = i + off - wl (wl >= 0; no bound when wl < 0) and
+ * hi = i + off + wr (wr >= 0; no bound when wr < 0).  Over the visible keys:
+ *   s_j = (sum_d q_d k_jd) * scale,  p_j = exp(s_j - max s) / sum exp(s - max s),
+ *   out_d = sum_j p_j v_jd;  out = 0 when no key is visible.
+ * rows: nrows triples (b, h, i); out: nrows x D doubles.
+ */
+int oracle_attn_rows_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int S_q,
+                        int S_kv, int H, int H_kv, int D, float scale, int wl, int wr,
+                        const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (B <= 0 || S_q <= 0 || S_kv <= 0 || H <= 0 || H_kv <= 0 || D <= 0 || nrows < 0 || H % H_kv)
+    return ORACLE_EINVAL;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= H ||
+        rows[3 * r + 2] < 0 || rows[3 * r + 2] >= S_q)
+      return ORACLE_EINVAL;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int G = H / H_kv;
+  const double sc = (double)scale;
+  int status = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)S_kv);
+    if (!s) {
+#pragma omp atomic write
+      status = ORACLE_ENOMEM;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (!s) continue;
+      const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+      const int64_t hk = h / G;
+      const int64_t off = (int64_t)S_kv - S_q;
+      int64_t lo = 0, hi = S_kv - 1;
+      if (wl >= 0 && i + off - wl > lo) lo = i + off - wl;
+      if (wr >= 0 && i + off + wr < hi) hi = i + off + wr;
+      for (int d = 0; d < D; ++d) out[r * D + d] = 0.0;
+      if (lo > hi) continue; /* no visible key */
+      double smax = -INFINITY;
+      for (int64_t j = lo; j <= hi; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+          dot += (double)bf16_to_f32(q[((b * S_q + i) * H + h) * D + d]) *
+                 (double)bf16_to_f32(k[((b * S_kv + j) * H_kv + hk) * D + d]);
+        s[j] = dot * sc;
+        if (s[j] > smax) smax = s[j];
+      }
+      double l = 0.0;
+      for (int64_t j = lo; j <= hi; ++j) {
+        s[j] = exp(s[j] - smax);
+        l += s[j];
+      }
+      for (int64_t j = lo; j <= hi; ++j)
+        for (int d = 0; d < D; ++d)
+          out[r * D + d] += (s[j] / l) * (double)bf16_to_f32(v[((b * S_kv + j) * H_kv + hk) * D + d]);
+    }
+    free(s);
+  }
+  return status;
 }

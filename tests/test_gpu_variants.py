@@ -1,0 +1,131 @@
+"""GPU checks of the attention variants through the C ABI, both modes, against
+the oracle's exact attention with a key window, S_q != S_kv and grouped heads
+("RDNAttention" README, "Features": cross-attention and decode, GQA/MQA, causal
+masking, one- and two-sided sliding windows).
+
+Gates as for self-attention (BF16: max abs <= 1e-2, cosine >= 0.99999; Sage:
+cosine >= 0.998, relative L2 <= 5e-2), over the rows that see at least one key;
+a row that sees none must be exactly zero.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import image_dit_amd as ia
+import oracle
+from image_dit_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+SCALE = float(np.float32(1 / math.sqrt(128)))
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def record(kind, name, mt):
+    path = os.environ.get("DITATTN_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(kind=kind, workload=name, **mt)) + "\n")
+
+
+def inputs(B, S_q, S_kv, H, H_kv, seed, k_bias_std=0.0):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, S_q, H, 128), generator=g)
+    k = torch.randn((B, S_kv, H_kv, 128), generator=g)
+    v = torch.randn((B, S_kv, H_kv, 128), generator=g)
+    if k_bias_std:
+        k += k_bias_std * torch.randn((H_kv, 128), generator=g)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def seen_rows(S_q, S_kv, wl, wr):
+    i = np.arange(S_q) + (S_kv - S_q)
+    lo = np.maximum(i - wl, 0) if wl >= 0 else np.zeros(S_q, dtype=np.int64)
+    hi = np.minimum(i + wr, S_kv - 1) if wr >= 0 else np.full(S_q, S_kv - 1)
+    return lo <= hi
+
+
+def check(name, got_gpu, q, k, v, window, rows):
+    """Compare the sampled rows (b, h, i) of got_gpu [B, S_q, H, 128] with the oracle."""
+    B, S_q, H, _ = q.shape
+    S_kv = k.shape[1]
+    ref = oracle.attn_rows_ex(q, k, v, SCALE, window, rows=rows)
+    idx = torch.from_numpy(rows).to(got_gpu.device)
+    got = got_gpu[idx[:, 0], idx[:, 2], idx[:, 1]].float().cpu().numpy().astype(np.float64)
+    seen = seen_rows(S_q, S_kv, *window)[rows[:, 2]]
+    assert np.all(np.isfinite(got))
+    assert not got[~seen].any(), "rows that see no key must be zero"
+    g, r = got[seen], ref[seen]
+    cos = float(np.sum(g * r) / (np.linalg.norm(g) * np.linalg.norm(r)))
+    rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    mt = dict(cos=cos, rel_l2=rel, max_abs=float(np.max(np.abs(g - r))), rows=int(seen.sum()),
+              empty_rows=int((~seen).sum()))
+    log("[%s] %s" % (name, mt))
+    return mt
+
+
+CASES = [  # B, S_q, S_kv, H, H_kv, (wl, wr)
+    (2, 300, 77, 4, 4, (-1, -1)),        # cross-attention to a short (text) sequence
+    (1, 64, 1000, 6, 1, (-1, -1)),       # MQA, S_q < S_kv
+    (1, 500, 500, 8, 2, (-1, -1)),       # GQA self-attention
+    (1, 1000, 1000, 2, 2, (-1, 0)),      # causal
+    (2, 700, 300, 2, 1, (-1, 0)),        # causal, S_q > S_kv: the first 400 rows see nothing
+    (1, 300, 700, 4, 2, (-1, 0)),        # causal, S_q < S_kv
+    (1, 1500, 1500, 2, 2, (128, 128)),   # two-sided sliding window
+    (1, 1200, 1200, 3, 3, (300, 0)),     # one-sided (causal) sliding window
+    (1, 333, 333, 2, 2, (0, 40)),        # window ahead of the query only
+    (3, 1, 5000, 4, 4, (-1, 0)),         # decode step: one query row sees every key
+    (1, 4608, 512, 24, 24, (-1, -1)),    # DiT cross-attention to text tokens, FLUX width
+    (1, 4608, 4608, 24, 24, (512, 512)), # windowed FLUX-1024 self-attention
+]
+
+
+def case_id(c):
+    B, S_q, S_kv, H, H_kv, w = c
+    return "B%d-q%d-kv%d-h%d-hkv%d-w%d_%d" % (B, S_q, S_kv, H, H_kv, w[0], w[1])
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("c", CASES, ids=[case_id(c) for c in CASES])
+def test_variant_both_modes(c):
+    B, S_q, S_kv, H, H_kv, window = c
+    name = case_id(c)
+    log("[variant %s]" % name)
+    q, k, v = inputs(B, S_q, S_kv, H, H_kv, seed=S_q + 3 * S_kv + H + H_kv, k_bias_std=2.0)
+    rows = synth.sample_rows(B, S_q, H, n=2048, seed=S_q + S_kv)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = ia.attn_fwd_bf16_ex(qd, kd, vd, SCALE, window)
+    torch.cuda.synchronize()
+    mt = check("bf16 " + name, out, q, k, v, window, rows)
+    record("bf16_variant", name, mt)
+    assert mt["max_abs"] <= 1e-2 and mt["cos"] >= 0.99999, mt
+    sout = ia.sage_attention_ex(qd, kd, vd, SCALE, window)
+    torch.cuda.synchronize()
+    ms = check("sage " + name, sout, q, k, v, window, rows)
+    record("sage_variant", name, ms)
+    assert ms["cos"] >= 0.998 and ms["rel_l2"] <= 5e-2, ms
+
+
+def test_ex_entry_points_equal_the_plain_ones():
+    # full window, S_q = S_kv, H_kv = H: the _ex calls are the plain calls, bit for bit
+    q, k, v = (t.cuda() for t in synth.make_qkv(2, 777, 3, seed=91))
+    assert torch.equal(ia.attn_fwd_bf16_ex(q, k, v, SCALE), ia.attn_fwd_bf16(q, k, v, SCALE))
+    assert torch.equal(ia.sage_attention_ex(q, k, v, SCALE), ia.sage_attention(q, k, v, SCALE))
+
+
+def test_windowed_variants_deterministic():
+    q, k, v = (t.cuda() for t in inputs(1, 900, 1300, 4, 2, seed=5))
+    for window in ((-1, 0), (100, 50)):
+        a = ia.attn_fwd_bf16_ex(q, k, v, SCALE, window)
+        b = ia.attn_fwd_bf16_ex(q, k, v, SCALE, window)
+        sa = ia.sage_attention_ex(q, k, v, SCALE, window)
+        sb = ia.sage_attention_ex(q, k, v, SCALE, window)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(sa, sb)

@@ -502,3 +502,67 @@ def test_smoothed_quant_matches_torch_vectorized():
     # smoothing shrinks the block scales of a K with per-channel bias
     _, plain = oracle.quant_qk(k, 1.0)
     assert float(scales[:, :, : S // 32].mean()) < 0.7 * float(plain[:, :, : S // 32].mean())
+
+
+# --------------------------------------------------------------------------
+# exact attention with S_q != S_kv, grouped heads and a key window
+# ("RDNAttention" README, "Features")
+# --------------------------------------------------------------------------
+
+def sdpa_masked_f64(q, k, v, scale, wl, wr):
+    """torch SDPA in float64 with an explicit boolean mask and K/V heads repeated."""
+    B, S_q, H, D = q.shape
+    S_kv, H_kv = k.shape[1], k.shape[2]
+    G = H // H_kv
+    qd = q.double().permute(0, 2, 1, 3)
+    kd = k.double().permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    vd = v.double().permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    i = torch.arange(S_q)[:, None] + (S_kv - S_q)
+    j = torch.arange(S_kv)[None, :]
+    mask = torch.ones((S_q, S_kv), dtype=torch.bool)
+    if wl >= 0:
+        mask &= j >= i - wl
+    if wr >= 0:
+        mask &= j <= i + wr
+    out = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=mask, scale=scale)
+    return out.permute(0, 2, 1, 3).numpy(), mask.any(dim=1).numpy()
+
+
+@pytest.mark.parametrize("S_q,S_kv,H,H_kv,wl,wr", [
+    (50, 50, 4, 4, -1, -1), (37, 90, 4, 2, -1, -1), (90, 37, 6, 1, -1, -1),   # cross, GQA, MQA
+    (70, 70, 2, 2, -1, 0), (40, 100, 2, 1, -1, 0), (100, 40, 2, 2, -1, 0),   # causal, aligned at the end
+    (80, 80, 2, 2, 9, 0), (80, 80, 4, 2, 7, 7), (60, 90, 2, 2, 0, 12), (1, 77, 3, 3, -1, 0)])
+def test_attn_rows_ex_matches_sdpa_with_mask(S_q, S_kv, H, H_kv, wl, wr):
+    g = torch.Generator().manual_seed(S_q * 7 + S_kv + wl + 3 * wr)
+    B = 2
+    q = torch.randn((B, S_q, H, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, S_kv, H_kv, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, S_kv, H_kv, 128), generator=g).to(torch.bfloat16)
+    got = oracle.attn_rows_ex(q, k, v, SCALE, (wl, wr))
+    ref, seen = sdpa_masked_f64(q, k, v, SCALE, wl, wr)
+    assert np.max(np.abs(got[:, seen] - ref[:, seen])) < 1e-12
+    assert not got[:, ~seen].any()  # rows that see no key are zero
+
+
+def test_attn_rows_ex_closed_forms():
+    B, S, H = 1, 64, 2
+    q, k, v = rand_qkv(B, S, H, seed=31)
+    # a window of one key returns that key's value
+    got = oracle.attn_rows_ex(q, k, v, SCALE, (0, 0))
+    assert np.array_equal(got, v.double().numpy())
+    # causal: the first query sees only the first key
+    got = oracle.attn_rows_ex(q, k, v, SCALE, (-1, 0))
+    assert np.array_equal(got[:, 0], v[:, 0].double().numpy())
+    # full window equals plain self-attention
+    assert np.max(np.abs(oracle.attn_rows_ex(q, k, v, SCALE) - oracle.attn_rows(q, k, v, SCALE))) < 1e-12
+    # a decode step (one query) under the causal mask sees every key
+    qd = q[:, -1:].contiguous()
+    a = oracle.attn_rows_ex(qd, k, v, SCALE, (-1, 0))
+    full = oracle.attn_rows(q, k, v, SCALE)[:, -1:]
+    assert np.max(np.abs(a - full)) < 1e-12
+    # single key/value head shared by every query head
+    k1, v1 = k[:, :, :1].contiguous(), v[:, :, :1].contiguous()
+    got = oracle.attn_rows_ex(q, k1, v1, SCALE)
+    for h in range(H):
+        ref = oracle.attn_rows(q[:, :, h:h + 1].contiguous(), k1, v1, SCALE)
+        assert np.max(np.abs(got[:, :, h:h + 1] - ref)) < 1e-12
