@@ -20,7 +20,7 @@ import os
 __all__ = ["DitAttnError", "load", "abi_version", "sage_padded_len", "sage_workspace_size",
            "attn_fwd_bf16", "attn_fwd_bf16_ex", "sage_prepare", "sage_prepare_ex",
            "qk_norm_rope_bf16", "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attention",
-           "sage_attention_ex", "HEAD_DIM", "LIB_PATH"]
+           "sage_attention_ex", "sage_prepare_ex_noalloc", "STATIC_SCRATCH_BYTES", "HEAD_DIM", "LIB_PATH"]
 
 HEAD_DIM = 128
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
@@ -57,11 +57,13 @@ def load(path=None):
                                                           ctypes.c_size_t, vp])
     lib.qk_norm_rope_bf16.argtypes = [vp, vp, ci, ci, ci, ci, vp, cf, vp, vp, ci, vp]
     lib.attn_fwd_bf16_ex.argtypes = [vp, vp, vp, vp] + [ci] * 6 + [cf, ci, ci, vp]
+    lib.sage_prepare_ex_noalloc.argtypes = [vp] * 9 + [ci] * 6 + [cf, vp, vp, cf, vp, vp, ci, vp, vp]
     lib.sage_attn_fwd_ex.argtypes = [vp] * 7 + [ci] * 6 + [cf, ci, ci, vp]
     lib.ditattn_sage_workspace_size.argtypes = [ci, ci, ci]
     lib.ditattn_sage_workspace_size.restype = ctypes.c_size_t
     for name in ("attn_fwd_bf16", "sage_prepare", "sage_attn_fwd", "sage_prepare_ex",
-                 "qk_norm_rope_bf16", "attn_fwd_bf16_ex", "sage_attn_fwd_ex"):
+                 "qk_norm_rope_bf16", "attn_fwd_bf16_ex", "sage_attn_fwd_ex",
+                 "sage_prepare_ex_noalloc"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -74,6 +76,9 @@ def _status(lib, func, st):
 
 def abi_version():
     return load().ditattn_abi_version()
+
+
+STATIC_SCRATCH_BYTES = 16 << 20  # the library's static device scratch (sage_prepare_ex_noalloc)
 
 
 def sage_padded_len(S):
@@ -292,6 +297,44 @@ def sage_prepare_ex(q, k, v, scale, q_norm_w=None, k_norm_w=None, norm_eps=1e-6,
                              _opt_ptr(k_mean), _opt_ptr(workspace), ws_bytes, _stream_handle(stream))
     _status(lib, "sage_prepare_ex", st)
     return tuple(out) + ((k_mean,) if smooth_k else ())
+
+
+def sage_prepare_ex_noalloc(q, k, v, scale, out, k_mean=None, q_norm_w=None, k_norm_w=None,
+                            norm_eps=1e-6, rope_cos=None, rope_sin=None, rope_dim=0, stream=None):
+    """sage_prepare_ex into caller-supplied outputs with no workspace: K smoothing
+    (k_mean given, fp32 [B, H_kv, 128]) uses the library's static device scratch.
+    The library allocates nothing; calls overlapping on one GPU race on that scratch."""
+    import torch
+    lib = load()
+    B, S_q, H, D = _dims(q)
+    _, S_kv, H_kv, _ = _dims(k)
+    _check_bshd("q", q, torch.bfloat16)
+    for name, t in (("k", k), ("v", v)):
+        _check_bshd(name, t, torch.bfloat16)
+        if tuple(t.shape) != (B, S_kv, H_kv, D):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S_kv, H_kv, D)))
+    dev = q.device
+    _check_small("q_norm_w", q_norm_w, (D,), torch.bfloat16, dev)
+    _check_small("k_norm_w", k_norm_w, (D,), torch.bfloat16, dev)
+    if rope_dim:
+        n_tab = max(S_q, S_kv)
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            if t is None or t.dim() != 2 or t.shape[0] < n_tab or t.shape[1] != rope_dim:
+                raise ValueError("%s must be [>= %d, %d]" % (name, n_tab, rope_dim))
+            _check_out(name, t, tuple(t.shape), torch.bfloat16, dev)
+    if out is None or len(out) != 6:
+        raise ValueError("out must be the 6 preallocated tensors of a sage_prepare_ex result")
+    for t, (name, shape, dt) in zip(out, _prepared_specs(B, S_q, H, D, S_kv, H_kv)):
+        _check_out(name, t, shape, dt, dev)
+    _check_small("k_mean", k_mean, (B, H_kv, D), torch.float32, dev)
+    st = lib.sage_prepare_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S_q,
+                                     S_kv, H, H_kv, D, float(scale), _opt_ptr(q_norm_w),
+                                     _opt_ptr(k_norm_w), float(norm_eps),
+                                     _opt_ptr(rope_cos if rope_dim else None),
+                                     _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
+                                     _opt_ptr(k_mean), _stream_handle(stream))
+    _status(lib, "sage_prepare_ex_noalloc", st)
+    return tuple(out) + ((k_mean,) if k_mean is not None else ())
 
 
 def qk_norm_rope_bf16(x, norm_w=None, norm_eps=1e-6, rope_cos=None, rope_sin=None, rope_dim=0,

@@ -5,8 +5,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/ditattn.h"
 #include "launch.hpp"
+
+// Device scratch of sage_prepare_ex_noalloc (the K-smoothing partial sums).  Each GPU
+// the library runs on holds its own copy until the process ends.  In host code the
+// name is only a stand-in: kernels get the device address from scratch_address().
+static __device__ __align__(256) unsigned char scratch[DITATTN_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -66,6 +73,26 @@ int check_xform(const void* norm_w0, const void* norm_w1, float eps, const void*
 
 float log2e_scale(float scale) { return static_cast<float>(static_cast<double>(scale) * kLog2eD); }
 
+// Device address of `scratch` on the current device, looked up on the first call on each
+// device and kept (the lookup allocates nothing; concurrent first calls store the same value).
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,6 +109,7 @@ const char* ditattn_status_string(int status) {
     case DITATTN_EALIGN: return "pointer not 16-byte aligned";
     case DITATTN_EOVERFLOW: return "size exceeds what the kernels index";
     case DITATTN_EHIP: return "HIP launch failed";
+    case DITATTN_ENOSPACE: return "K smoothing needs more scratch than the static buffer holds (DITATTN_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -167,6 +195,28 @@ int sage_prepare_ex(const void* q, const void* k, const void* v, int8_t* q_i8, f
                          k_mean, workspace};
   if (ditattn::launch_sage_prepare(a, stream) != hipSuccess) return DITATTN_EHIP;
   return DITATTN_OK;
+}
+
+int sage_prepare_ex_noalloc(const void* q, const void* k, const void* v, int8_t* q_i8,
+                            float* q_scale, int8_t* k_i8, float* k_scale, uint8_t* v_fp8,
+                            float* v_scale, int B, int S_q, int S_kv, int H, int H_kv, int D,
+                            float scale, const void* q_norm_w, const void* k_norm_w,
+                            float norm_eps, const void* rope_cos, const void* rope_sin,
+                            int rope_dim, float* k_mean, hipStream_t stream) {
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (k_mean) {
+    // the size check touches no GPU; the shapes themselves are checked by sage_prepare_ex
+    const int st = check_sizes(B, S_q, S_kv, H, H_kv, D, scale);
+    if (st != DITATTN_OK) return st;
+    if (ditattn::sage_workspace_bytes(B, S_kv, H_kv) > DITATTN_STATIC_SCRATCH_BYTES)
+      return DITATTN_ENOSPACE;
+    if (scratch_address(&ws) != hipSuccess) return DITATTN_EHIP;
+    ws_bytes = DITATTN_STATIC_SCRATCH_BYTES;
+  }
+  return sage_prepare_ex(q, k, v, q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, B, S_q, S_kv, H,
+                         H_kv, D, scale, q_norm_w, k_norm_w, norm_eps, rope_cos, rope_sin,
+                         rope_dim, k_mean, ws, ws_bytes, stream);
 }
 
 int sage_prepare(const void* q, const void* k, const void* v, int8_t* q_i8, float* q_scale,

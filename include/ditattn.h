@@ -60,6 +60,8 @@ typedef struct ihipStream_t* hipStream_t;
 /* Size limits (see the conventions above). */
 #define DITATTN_MAX_HEADS 65536
 #define DITATTN_MAX_SEQ_SAGE (1 << 25)
+/* Size of the library's static device scratch (sage_prepare_ex_noalloc). */
+#define DITATTN_STATIC_SCRATCH_BYTES (16u << 20)
 
 /* Status codes. */
 #define DITATTN_OK 0
@@ -69,6 +71,7 @@ typedef struct ihipStream_t* hipStream_t;
 #define DITATTN_EALIGN (-3)       /* a pointer is not 16-byte aligned */
 #define DITATTN_EOVERFLOW (-4)    /* a byte size or the grid exceeds what the kernels index */
 #define DITATTN_EHIP (-5)         /* the HIP runtime rejected a launch */
+#define DITATTN_ENOSPACE (-6)     /* sage_prepare_ex_noalloc: scratch needed > DITATTN_STATIC_SCRATCH_BYTES */
 
 /* DITATTN_ABI_VERSION of the loaded library. */
 int ditattn_abi_version(void);
@@ -194,6 +197,27 @@ int sage_prepare_ex(const void* q, const void* k, const void* v, int8_t* q_i8, f
                     const void* k_norm_w, float norm_eps, const void* rope_cos,
                     const void* rope_sin, int rope_dim, float* k_mean, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sage_prepare_ex_noalloc -- sage_prepare_ex without the workspace arguments, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  It allocates nothing: K
+ * smoothing (k_mean != NULL) uses a static device buffer of the library,
+ * DITATTN_STATIC_SCRATCH_BYTES per GPU, and returns DITATTN_ENOSPACE before
+ * anything is enqueued when ditattn_sage_workspace_size(B, S_kv, H_kv) exceeds
+ * it.  The buffer's contents on entry do not matter (every value read is
+ * written earlier in the same call).  Every call on one GPU shares that GPU's
+ * buffer: calls that may overlap on one GPU (other streams, other threads) race.
+ * The buffer's device address is looked up on the first smoothing call on each
+ * device; make that first call outside graph capture.  Results are bit for bit
+ * those of sage_prepare_ex.
+ */
+int sage_prepare_ex_noalloc(const void* q, const void* k, const void* v, int8_t* q_i8,
+                            float* q_scale, int8_t* k_i8, float* k_scale, uint8_t* v_fp8,
+                            float* v_scale, int B, int S_q, int S_kv, int H, int H_kv, int D,
+                            float scale, const void* q_norm_w, const void* k_norm_w,
+                            float norm_eps, const void* rope_cos, const void* rope_sin,
+                            int rope_dim, float* k_mean, hipStream_t stream);
 
 /* Workspace bytes sage_prepare_ex needs for K smoothing at these sizes (0 for
  * sizes it rejects).  Touches no GPU. */

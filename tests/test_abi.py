@@ -288,3 +288,32 @@ def test_qk_norm_rope_rejects(lib):
     assert call(eps=float("nan"), w=W) == EINVAL
     assert call(out=GOOD + 256) == EINVAL  # partial overlap; exact in-place is allowed
     assert call(w=GOOD * 2 ** 30 + 1024) == EINVAL  # weight inside the output
+
+
+# ---------------------------------------------------------------- sage_prepare_ex_noalloc
+ENOSPACE = -6
+
+
+def test_static_scratch_size_matches_header():
+    m = re.search(r"#define DITATTN_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == ia.STATIC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    vp = ctypes.c_void_p
+    W = GOOD * 2 ** 40
+
+    def call(B=1, S=100, H=2, H_kv=2, k_mean=None):
+        ptrs = [GOOD * 2 ** (20 + i) for i in range(9)]
+        return lib.sage_prepare_ex_noalloc(*[vp(p) for p in ptrs], B, S, S, H, H_kv, 128,
+                                           ctypes.c_float(0.088), None, None, ctypes.c_float(1e-6),
+                                           None, None, 0, vp(k_mean), None)
+    lib.ditattn_sage_workspace_size.restype = ctypes.c_size_t
+    # smoothing whose partial sums exceed the static scratch: B*H rows of one token range each
+    B, S, H = 128, 16, 256
+    assert lib.ditattn_sage_workspace_size(B, S, H) > ia.STATIC_SCRATCH_BYTES
+    assert call(B=B, S=S, H=H, H_kv=H, k_mean=W) == ENOSPACE
+    assert "scratch" in lib.ditattn_status_string(ENOSPACE).decode()
+    # argument errors come first, as in sage_prepare_ex
+    assert call(H=3, H_kv=2, k_mean=W) == EINVAL
+    assert call(H=3, H_kv=2) == EINVAL
