@@ -47,6 +47,7 @@ MODES = ("bf16", "sage", "sage_core", "prepare")
 # largest first; the FLUX-1024 rows last, right before the headline at that shape
 DEFAULT_ROWS = ["wan720p:bf16", "wan720p:sage", "wan720p:sage_core", "wan720p:prepare",
                 "flux2048:bf16", "flux2048:sage", "flux2048:sage_core", "flux2048:prepare",
+                "hunyuan720p:bf16", "hunyuan720p:sage", "hunyuan720p:sage_core", "hunyuan720p:prepare",
                 "flux1024:prepare", "flux1024:sage_core", "flux1024:sage"]
 
 

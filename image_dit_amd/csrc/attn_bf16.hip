@@ -1,15 +1,17 @@
-// attn_bf16.hip -- BF16 flash self-attention forward for gfx950 (MI355X).
+// attn_bf16.hip -- BF16 flash attention forward for gfx950 (MI355X).
 //
 // Operation: "Kernel acceleration: attention, compilation and fusion",
 // section "Attention: from O(N^2) memory to blocks" -- attention computed one
 // key block at a time with a running row max m, running row sum l and an
-// accumulator rescaled by exp(m_old - m_new), so the S x S scores never leave
-// the chip.  Shape contract (BF16 [B, S, H, 128] in and out, non-causal) from
-// "gfx1201_sage_prepare / gfx1201_sage_attention", "Technical Details".
+// accumulator rescaled by exp(m_old - m_new), so the S_q x S_kv scores never
+// leave the chip.  Shape contract (BF16 [B, S, H, 128] in and out) from
+// "gfx1201_sage_prepare / gfx1201_sage_attention", "Technical Details";
+// cross-attention (S_q != S_kv), grouped-query heads (H_kv | H) and key
+// windows (causal / sliding, bottom-right aligned) generalise it.
 //
 // gfx950 mapping
-//   * Work unit: one workgroup per (b, h, BQ-row query tile); 4 waves, each
-//     owning 32 * QG query rows.  Workgroups are remapped so one head's tiles
+//   * Work unit: one workgroup of 8 waves per (b, h, 256-row query tile), each
+//     wave owning 32 query rows.  Workgroups are remapped so one head's tiles
 //     share an XCD (and its L2) while they stream the same K/V.
 //   * Scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 channels read from LDS,
@@ -22,18 +24,26 @@
 //     so P never goes through LDS.  The A operand V^T (channels x keys) is read
 //     from the row-major V tile with ds_read_b64_tr_b16, which transposes 16-bit
 //     elements inside groups of 16 lanes.
-//   * K/V tiles of BK = 64 keys are double-buffered in LDS (one barrier per
-//     tile).  Rows are 256 B, unpadded, with 16-byte chunks XOR-swizzled per row
-//     so that both the MFMA-operand reads and the transposed reads are free of
-//     bank conflicts.
+//   * K/V tiles of 64 keys are double-buffered in LDS.  Rows are 256 B,
+//     unpadded, with 16-byte chunks XOR-swizzled per row so that both the
+//     MFMA-operand reads and the transposed reads are free of bank conflicts.
+//   * Ping-pong: waves w and w + 4 share a SIMD and run the same phase sequence
+//     one barrier apart, so one wave's matrix phase (P V of the previous tile,
+//     K Q^T of this one: 32 MFMA) overlaps the other's softmax (VALU).
+//   * Copies: only the first four waves copy, eight 1 KB buffer_load ... lds
+//     per wave per tile, one after every second MFMA of their matrix phase, so
+//     the address unit (about 64 B per clock per CU) drains while the matrix
+//     core works instead of stalling every wave at the same barrier.  The
+//     buffer resource ends after the last key: rows past it in a ragged last
+//     tile read as zeros, and their scores are masked to -inf.
 //   * Softmax in base 2: x = s * c with c = scale * log2(e); exp2 on v_exp_f32.
 //     The running max is only raised when a row's tile max exceeds it by more
 //     than kLazyThresh (in log2 units): P values up to 2^kLazyThresh are
-//     harmless in BF16/FP32, and the O rescale (64 multiplies per lane and
-//     query group) is skipped on almost every tile.  The result is the same
-//     math: every p and l use the same stale max, which cancels in acc / l.
-//   * Ragged tail: key rows >= S are zero-filled in LDS and their scores set to
-//     -inf; query rows >= S are computed on zeros and not stored.
+//     harmless in BF16/FP32, and the O rescale (64 multiplies per lane) is
+//     skipped on almost every tile.  Every p and l use the same stale max,
+//     which cancels in acc / l.
+//   * Query rows >= S_q are computed on zeros and not stored; rows that see no
+//     key (an empty window) are written as zeros.
 #include <type_traits>
 
 #include "common.hpp"
@@ -53,8 +63,6 @@ namespace bf16attn {
 
 constexpr int BK = 64;      // keys per K/V tile
 constexpr int NW = DITATTN_BF16_NW;
-constexpr int RPW = BK / NW;   // tile rows each wave copies
-constexpr int NCP = RPW / 4;   // 1 KB copy instructions per wave per tile (K or V)
 static_assert(NW == 8, "the ping-pong pairs waves w and w + 4 on one SIMD");
 constexpr float kLazyThresh = 8.0f;
 
@@ -128,35 +136,50 @@ attn_fwd_bf16_kernel(Bf16Args a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-  // ---- global -> LDS (direct).  Wave w, instruction n writes LDS rows RPW w + 4 n + l / 16,
-  // physical chunk l % 16; the lane fetches the logical chunk that lands there.
+  // ---- global -> LDS (direct).  Instruction n of a copying wave writes LDS rows
+  // 16 w + 4 n + l / 16, physical chunk l % 16; the lane fetches the logical chunk
+  // that lands there.
   const int p_chunk = l & 15;
-  uint32_t koff[NCP], voff[NCP];  // this lane's source offsets in a full tile
+  // Group-A copies: wave w (< NW / 2) copies rows 16 w .. 16 w + 15 of each tile, four
+  // 1 KB instructions, instruction n covering rows 16 w + 4 n + l / 16.
+  uint32_t akoff[4], avoff[4];
 #pragma unroll
-  for (int n = 0; n < NCP; ++n) {
-    const int r = RPW * wave + 4 * n + (l >> 4);
-    koff[n] = r * tok_bytes + 16u * (uint32_t)(p_chunk ^ (r & 15));
-    voff[n] = r * tok_bytes + 16u * (uint32_t)(p_chunk ^ ((r & 3) << 2));
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * (wave & 3) + 4 * i + (l >> 4);
+    akoff[i] = r * tok_bytes + 16u * (uint32_t)(p_chunk ^ (r & 15));
+    avoff[i] = r * tok_bytes + 16u * (uint32_t)(p_chunk ^ ((r & 3) << 2));
   }
-  // Copy key tile t of K (is_v false) or V (is_v true) into the LDS stage at byte
-  // offset dst.  In the ragged last tile, rows past the end repeat the last real
-  // key: finite data whose scores are masked to -inf (so P = 0 against it).
-  const int n_kt = (a.S_kv + BK - 1) / BK;
-  const bool ragged = (a.S_kv % BK) != 0;
-  auto issue = [&](const char* src, int t, int dst, bool is_v) {
-    const int j0 = t * BK;
-    const char* st = src + (int64_t)j0 * tok_kv * 2;
-    const bool clamp = ragged && t == n_kt - 1;
-#pragma unroll
-    for (int n = 0; n < NCP; ++n) {
-      uint32_t off = is_v ? voff[n] : koff[n];
-      if (clamp) {
-        const int r = RPW * wave + 4 * n + (l >> 4);
-        const int rr = (j0 + r >= a.S_kv) ? a.S_kv - 1 - j0 : r;
-        off = rr * tok_bytes + 16u * (uint32_t)(p_chunk ^ (is_v ? (r & 3) << 2 : r & 15));
-      }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(st + off),
-                                       (DITATTN_LDS void*)(lds + dst + (RPW * wave + 4 * n) * 256), 16, 0, 0);
+  // One period's copies: K(q+1) and V(q) (local tile indices), where they exist.
+  struct CopyPlan {
+    __amdgpu_buffer_rsrc_t rk, rv;  // K(q+1) and V(q)
+    int kdst, vdst;                 // LDS byte offsets of this wave's first rows
+    bool k_ok, v_ok;
+  };
+  auto plan = [&](int q) {
+    CopyPlan c;
+    auto rsrc = [&](const char* src, int tl) {
+      const int j0 = (t0 + tl) * BK;
+      const int rows = min(a.S_kv - j0, BK);
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(src + (int64_t)j0 * tok_kv * 2), (short)0,
+                                               (rows - 1) * (int)tok_bytes + 256, 0x00020000);
+    };
+    c.k_ok = q + 1 < n;
+    c.v_ok = q >= 0 && q < n;
+    c.rk = rsrc(kbh, c.k_ok ? q + 1 : 0);
+    c.rv = rsrc(vbh, c.v_ok ? q : 0);
+    c.kdst = K_STAGE0 + ((q + 1) & 1) * TILE_BYTES + 16 * (wave & 3) * 256;
+    c.vdst = V_STAGE0 + (q & 1) * TILE_BYTES + 16 * (wave & 3) * 256;
+    return c;
+  };
+  // instruction j (0..7) of a copy plan: j < 4 -> part j of K(q+1), else part j - 4 of V(q)
+  auto copy_part = [&](const CopyPlan& c, int j) {
+    const int i = j & 3;
+    if (j < 4) {
+      if (c.k_ok)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rk, (DITATTN_LDS void*)(lds + c.kdst + 4 * i * 256), 16, akoff[i], 0, 0, 0);
+    } else {
+      if (c.v_ok)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rv, (DITATTN_LDS void*)(lds + c.vdst + 4 * i * 256), 16, avoff[i], 0, 0, 0);
     }
   };
 
@@ -184,7 +207,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // under the last P V chunks.  Waits count outstanding LDS reads (returned in order).
   f32x16 sc[2];  // scores of the latest tile, one 32-key sub-tile each
   bf16x8 pf[4];  // P of the latest softmax, one 16-key chunk each
-  auto mphase = [&](auto vs_c, auto ks_c, auto pv_c, auto qk_c) {
+  auto mphase = [&](auto vs_c, auto ks_c, auto pv_c, auto qk_c, int cq) {
+    const bool cp = cq >= 0;
+    const CopyPlan cpl = plan(cp ? cq : 0);
     constexpr int VS = decltype(vs_c)::value, KS = decltype(ks_c)::value;
     constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
     constexpr int VB = V_STAGE0 + VS * TILE_BYTES, KB = K_STAGE0 + KS * TILE_BYTES;
@@ -217,6 +242,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
         for (int dt = 0; dt < 4; ++dt) {
           const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{f[dt][0][0], f[dt][0][1], f[dt][1][0], f[dt][1][1]});
           acc[dt] = mfma_bf16_32x32x16(va, pf[cc], acc[dt]);
+          if (dt & 1) {
+            if (cp) copy_part(cpl, 2 * cc + (dt >> 1));
+          }
         }
       };
       vread(C0{}, fa);
@@ -252,6 +280,9 @@ attn_fwd_bf16_kernel(Bf16Args a) {
         lds_wait<later>(kf[st][0], kf[st][1]);
         sc[0] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, kf[st][0]), qf[st], sc[0]);
         sc[1] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, kf[st][1]), qf[st], sc[1]);
+        if constexpr (!PV) {
+          if (cp) copy_part(cpl, st);
+        }
         kread(std::integral_constant<int, st + 3>{});
       };
       step(C0{});
@@ -327,15 +358,11 @@ attn_fwd_bf16_kernel(Bf16Args a) {
   // V(p) = softmax of tile p (VALU).  Group B (waves 4-7) starts one barrier late,
   // so on each SIMD one wave's matrix phase overlaps the other's softmax.
   // Barrier k: group A has finished phase k-1 of its sequence, group B phase k-2.
-  // K(q+1) and V(q) are copied in the window between barriers 2q and 2q+2 (issued
-  // at its start, awaited at its end): the stages they overwrite (K(q-1), V(q-2))
-  // were last read in M(q-1), which both groups finished by barrier 2q, and their
-  // first readers (M(q+1) of group A) start at barrier 2q+2.
+  // Group A copies K(q+1) and V(q) during its M(q) (after barrier 2q) and waits for
+  // them at the end of its V(q) (before barrier 2q+2): the stages they overwrite
+  // (K(q-1), V(q-2)) were last read in M(q-1), which both groups finished by barrier
+  // 2q, and their first readers (M(q+1) of group A) start at barrier 2q+2.
   const bool grp_a = wave < NW / 2;
-  auto copy = [&](int q) {  // K(q+1) and V(q) (local tile indices), where they exist
-    if (q + 1 < n) issue(kbh, t0 + q + 1, K_STAGE0 + ((q + 1) & 1) * TILE_BYTES, false);
-    if (q < n) issue(vbh, t0 + q, V_STAGE0 + (q & 1) * TILE_BYTES, true);
-  };
   auto copies_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   // s_barrier without the release fence of __syncthreads(), which would also wait
   // for the copies in flight; LDS reads before it have all been consumed.
@@ -349,30 +376,27 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     constexpr int par = decltype(par_c)::value;
     using KS = std::integral_constant<int, par>;
     using VS = std::integral_constant<int, par ^ 1>;
-    if (grp_a) copy(p);  // window 2p .. 2p+2
-    mphase(VS{}, KS{}, T{}, T{});
-    if (!grp_a) copies_landed();
+    mphase(VS{}, KS{}, T{}, T{}, grp_a ? p : -1);
     barrier();
-    if (!grp_a) copy(p + 1);  // window 2p+2 .. 2p+4
     softmax(t0 + p);
     if (grp_a) copies_landed();
     barrier();
   };
 
   if (n > 0) {  // uniform: every wave of the workgroup takes the same path
-  issue(kbh, t0, K_STAGE0, false);
-  copies_landed();
+  if (grp_a) {  // K(0)
+    const CopyPlan c0 = plan(-1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy_part(c0, j);
+    copies_landed();
+  }
   barrier();  // barrier 0
   if (!grp_a) {
-    copy(0);
     barrier();  // group B's leading barrier (barrier 1 for group A)
   }
   // period 0: no P V yet
-  if (grp_a) copy(0);
-  mphase(I0{}, I0{}, F{}, T{});
-  if (!grp_a) copies_landed();
+  mphase(I0{}, I0{}, F{}, T{}, grp_a ? 0 : -1);
   barrier();
-  if (!grp_a) copy(1);
   softmax(t0);
   if (grp_a) copies_landed();
   barrier();
@@ -386,8 +410,8 @@ attn_fwd_bf16_kernel(Bf16Args a) {
     ++p;
   }
   // M(n): P V of the last tile only
-  if (p & 1) mphase(I0{}, I0{}, T{}, F{});
-  else mphase(I1{}, I0{}, T{}, F{});
+  if (p & 1) mphase(I0{}, I0{}, T{}, F{}, -1);
+  else mphase(I1{}, I0{}, T{}, F{}, -1);
   if (grp_a) barrier();  // matches group B's leading barrier
   }
 
