@@ -33,10 +33,14 @@
 //     here and the vector unit has none, and numerator and denominator then
 //     use the same rounded P.  O = acc * v_scale / l.
 //   * Two wave groups ping-pong on each SIMD (waves w and w + 4 share one):
-//     one group's matrix phase (P V of the previous tile, K Q^T of this one)
-//     runs under the other group's softmax.  The softmax is the longer phase:
-//     a single wave issues at most one vector instruction every few cycles, so
-//     the phase is bound by that issue rate, not by the vector unit's width.
+//     one group's matrix phase (K Q^T of this tile, then P V of the previous
+//     one, under which the new scores are masked and their row max taken) runs
+//     under the other group's softmax.  Both phases are issue-bound: a single
+//     wave issues at most one vector instruction every few cycles and reads
+//     LDS at roughly 1 KB per 40 cycles, so each phase is bound by one wave's
+//     issue and LDS rates, not by the vector unit's width.  Only one wave per
+//     SIMD uses the matrix core at a time: splitting P V into the softmax
+//     phase was measured slower (the two waves' MFMA chains then collide).
 //   * Masks: keys j >= S_kv (zero codes, which would score 0) and keys outside
 //     a query's window get p = 0.  Only tiles that cross a mask boundary for
 //     some row of the workgroup take the masked path; a row with no visible
@@ -184,21 +188,16 @@ sage_attn_fwd_kernel(SageArgs a) {
     float s_tile;  // q_scale * k_scale of the half-wave's 32-key block in that tile
     // ---- matrix phase: O^T += V^T P^T (and the row sums) for V stage VS (4 + 1 MFMA) and/or
     // S^T = K Q^T for K stage KS (8 MFMA).
-    auto mphase = [&](auto vs_c, auto ks_c, auto pv_c, auto qk_c) __attribute__((always_inline)) {
+    float mx_tile;  // row max (scaled, log2 units) of the latest K Q^T, -inf where all hidden
+    constexpr int kMasked = INT32_MIN;  // no real score gets there: |acc| <= 128 * 127^2
+    // ---- matrix phase: S^T = K Q^T for K stage KS (8 MFMA), then O^T += V^T P^T (and the
+    // row sums) for V stage VS (4 + 1 MFMA); under the P V products the new scores are
+    // masked (tiles crossing a mask boundary) and their row max taken.
+    auto mphase = [&](auto vs_c, auto ks_c, auto pv_c, auto qk_c, int t) __attribute__((always_inline)) {
       constexpr int VS = decltype(vs_c)::value, KS = decltype(ks_c)::value;
       constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
       const DITATTN_LDS char* kb = (const DITATTN_LDS char*)(lds + K_STAGE0 + KS * KT_BYTES);
       const DITATTN_LDS char* vb = (const DITATTN_LDS char*)(lds + V_STAGE0 + VS * VT_BYTES);
-      if constexpr (PV) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const i32x4 v0 = *(const DITATTN_LDS i32x4*)(vb + vofs[0] + dt * 32 * 64);
-          const i32x4 v1 = *(const DITATTN_LDS i32x4*)(vb + vofs[1] + dt * 32 * 64);
-          const i32x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[dt] = mfma_fp8_32x32x64(va, pf, acc[dt], unit_scale);
-        }
-        lacc = mfma_fp8_32x32x64(ones, pf, lacc, unit_scale);
-      }
       if constexpr (QK) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -211,8 +210,46 @@ sage_attn_fwd_kernel(SageArgs a) {
         // read with the K rows: the stage is refilled one window later, while the
         // other group may still be in this tile's softmax
         s_tile = sq * *(const DITATTN_LDS float*)(lds + KS_STAGE0 + KS * 16 + 4 * hl);
+      }
+      if constexpr (PV) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const i32x4 v0 = *(const DITATTN_LDS i32x4*)(vb + vofs[0] + dt * 32 * 64);
+          const i32x4 v1 = *(const DITATTN_LDS i32x4*)(vb + vofs[1] + dt * 32 * 64);
+          const i32x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[dt] = mfma_fp8_32x32x64(va, pf, acc[dt], unit_scale);
+        }
+        lacc = mfma_fp8_32x32x64(ones, pf, lacc, unit_scale);
+      }
+      if constexpr (QK) {
+        if (masked_tile(t)) {
+          // keys t * BK + 32 hl + e, e = 16 tt + r, visible for e in [elo, ehi]
+          const int elo = lo_i - (t * BK + 32 * hl), ehi = hi_i - (t * BK + 32 * hl);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int e = 16 * tt + r;
+              si[tt][r] = (e < elo || e > ehi) ? kMasked : si[tt][r];
+            }
+        }
+        // row max on the biased int32 patterns (positive floats order like their bits), as a
+        // tree of v_max3_i32 for a short dependency chain
+        int m8[11];
+#pragma unroll
+        for (int j = 0; j < 10; ++j) {
+          const int e = 3 * j;
+          m8[j] = max(max(si[e >> 4][e & 15], si[(e + 1) >> 4][(e + 1) & 15]), si[(e + 2) >> 4][(e + 2) & 15]);
+        }
+        m8[10] = max(si[1][14], si[1][15]);
+        const int mi = max(max(max(max(m8[0], m8[1]), m8[2]), max(max(m8[3], m8[4]), m8[5])),
+                           max(max(max(m8[6], m8[7]), m8[8]), max(m8[9], m8[10])));
+        // s >= 0: scaling keeps the max; a half-wave with every key hidden contributes -inf
+        const float mh = mi == kMasked ? -INFINITY : (__int_as_float(mi) - kSeed) * s_tile;
+        mx_tile = half_pair_max(mh);
         pin(si[0]);
         pin(si[1]);
+        pin(mx_tile);
       }
       if constexpr (PV) {
 #pragma unroll
@@ -227,33 +264,8 @@ sage_attn_fwd_kernel(SageArgs a) {
     // hidden scores become INT32_MIN before the row max, and their p become 0 after exp2.
     auto softmax = [&](int t) __attribute__((always_inline)) {
       const float s = s_tile;
-      constexpr int kMasked = INT32_MIN;  // no real score gets there: |acc| <= 128 * 127^2
       const bool masked = masked_tile(t);  // uniform
-      if (masked) {
-        // keys t * BK + 32 hl + e, e = 16 tt + r, visible for e in [elo, ehi]
-        const int elo = lo_i - (t * BK + 32 * hl), ehi = hi_i - (t * BK + 32 * hl);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int e = 16 * tt + r;
-            si[tt][r] = (e < elo || e > ehi) ? kMasked : si[tt][r];
-          }
-      }
-      // row max on the biased int32 patterns (positive floats order like their bits), as a
-      // tree of v_max3_i32 for a short dependency chain
-      int m8[11];
-#pragma unroll
-      for (int j = 0; j < 10; ++j) {
-        const int e = 3 * j;
-        m8[j] = max(max(si[e >> 4][e & 15], si[(e + 1) >> 4][(e + 1) & 15]), si[(e + 2) >> 4][(e + 2) & 15]);
-      }
-      m8[10] = max(si[1][14], si[1][15]);
-      const int mi = max(max(max(max(m8[0], m8[1]), m8[2]), max(max(m8[3], m8[4]), m8[5])),
-                         max(max(max(m8[6], m8[7]), m8[8]), max(m8[9], m8[10])));
-      // s >= 0: scaling keeps the max; a half-wave with every key hidden contributes -inf
-      float mx = mi == kMasked ? -INFINITY : (__int_as_float(mi) - kSeed) * s;
-      mx = half_pair_max(mx);
+      const float mx = mx_tile;
       if (__builtin_amdgcn_ballot_w64(mx > m + kLazyThresh) != 0) {
         const float m_new = fmaxf(m, mx);
         const float alpha = m_new == m ? 1.0f : fast_exp2(m - m_new);
@@ -289,7 +301,6 @@ sage_attn_fwd_kernel(SageArgs a) {
       // exponentials past the barrier, next to the P V products that consume them
       asm volatile("" : "+v"(pf));
     };
-    auto softmax_tile = [&](int t) __attribute__((always_inline)) { softmax(t); };
 
     // ---- ping-pong over key tiles t0 .. t1 - 1 (local index p = t - t0), as in the BF16
     // kernel.  Waves w and w + 4 share a SIMD.  Every wave runs
@@ -338,10 +349,10 @@ sage_attn_fwd_kernel(SageArgs a) {
       using KS = std::integral_constant<int, st>;
       using VS = std::integral_constant<int, (st + NSTAGE - 1) % NSTAGE>;
       copy(p);
-      mphase(VS{}, KS{}, T{}, T{});
+      mphase(VS{}, KS{}, T{}, T{}, t0 + p);
       if (!grp_a) prev_landed(p);
       barrier();
-      softmax_tile(t0 + p);
+      softmax(t0 + p);
       if (grp_a) prev_landed(p);
       barrier();
     };
@@ -354,9 +365,9 @@ sage_attn_fwd_kernel(SageArgs a) {
     if (!grp_a) barrier();  // group B's leading barrier (barrier 1 for group A)
     // period 0: no P V yet, no window before it to wait for
     copy(0);
-    mphase(I0{}, I0{}, F{}, T{});
+    mphase(I0{}, I0{}, F{}, T{}, t0);
     barrier();
-    softmax_tile(t0);
+    softmax(t0);
     barrier();
     int p = 1;
     for (; p + 2 < n; p += 3) {  // three periods per trip: stage offsets are immediates
@@ -375,9 +386,9 @@ sage_attn_fwd_kernel(SageArgs a) {
     // M(n): P V of the last tile (n - 1) from V stage (n - 1) % 3
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int vs_last = (n - 1) % NSTAGE;
-    if (vs_last == 0) mphase(I0{}, I0{}, T{}, F{});
-    else if (vs_last == 1) mphase(I1{}, I0{}, T{}, F{});
-    else mphase(I2{}, I0{}, T{}, F{});
+    if (vs_last == 0) mphase(I0{}, I0{}, T{}, F{}, 0);
+    else if (vs_last == 1) mphase(I1{}, I0{}, T{}, F{}, 0);
+    else mphase(I2{}, I0{}, T{}, F{}, 0);
     if (grp_a) barrier();  // matches group B's leading barrier
   }
 
