@@ -39,6 +39,21 @@ constexpr uint32_t kAmaxFlag = 0x80000000u;  // bit 31 marks a running absmax wo
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// y / s rounded to nearest, as the correctly rounded division, from inv = 1 / s (itself
+// correctly rounded, computed once per scale): q0 = y * inv is within one ulp of y / s,
+// the residual y - q0 s is exact in one FMA, and q0 + r * inv then rounds to y / s
+// (Markstein's theorem on division by FMA).  It needs the residual not to underflow:
+// callers use it for 2^-60 <= s <= 2^100 (fast_div_ok) and divide otherwise.  The sign
+// is copied from y so that y = -0 gives -0 as the division does.  Checked against the
+// division on the GPU for every float32 quotient of magnitude 2^-12 .. 1024 and 64
+// divisors between 2^-63 and 2^120.
+__device__ __forceinline__ bool fast_div_ok(float s) { return s >= 0x1p-60f && s <= 0x1p100f; }
+__device__ __forceinline__ float div_by_recip(float y, float s, float inv) {
+  const float q0 = y * inv;
+  const float r = fmaf(-q0, s, y);
+  return __builtin_copysignf(fmaf(r, inv, q0), y);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
@@ -178,12 +193,21 @@ quant_qk_kernel(QuantSide qs, QuantSide ks, uint32_t* __restrict__ amax_bits, in
   }
   amax = wave_max(amax);
   const float s = amax / 127.0f;
+  const bool fast = fast_div_ok(s);
+  const float inv = 1.0f / s;
   int8_t* dst = a.codes + ((int64_t)bh * a.nblk * 32 + blk * 32) * kHeadDim;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int r = (lane >> 4) + 4 * p;
     uint32_t packed[2] = {0u, 0u};
-    if (s != 0.0f) {
+    if (fast) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float qv = rintf(div_by_recip(y[p][e], s, inv));
+        qv = fminf(fmaxf(qv, -127.0f), 127.0f);
+        packed[e >> 2] |= ((uint32_t)(int)qv & 0xFFu) << (8 * (e & 3));
+      }
+    } else if (s != 0.0f) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float qv = rintf(y[p][e] / s);
@@ -387,6 +411,25 @@ v_quant_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits,
       x[u][2 * e + 1] = bf16_bits_to_f32(w[e] >> 16);
     }
   }
+  bool fast = true;
+  float inv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    fast = fast && fast_div_ok(sv[e]);
+    inv[e] = 1.0f / sv[e];
+  }
+  // x / v_scale, 0 for tokens >= S (their codes are the zero padding)
+  if (fast) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[u][e] = div_by_recip(x[u][e], sv[e], inv[e]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[u][e] = sv[e] != 0.0f ? x[u][e] / sv[e] : 0.0f;
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {  // channel 8 * chunk + e, tokens 8 tg + 0..7
     uint32_t word[2];
@@ -396,7 +439,7 @@ v_quant_kernel(const uint16_t* __restrict__ v, uint32_t* __restrict__ amax_bits,
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = j0 + 8 * tg + 4 * half + u;
-        a[u] = (j < S && sv[e] != 0.0f) ? x[4 * half + u][e] / sv[e] : 0.0f;
+        a[u] = j < S ? x[4 * half + u][e] : 0.0f;
       }
       int wv = __builtin_amdgcn_cvt_pk_fp8_f32(a[0], a[1], 0, false);
       wv = __builtin_amdgcn_cvt_pk_fp8_f32(a[2], a[3], wv, true);
