@@ -155,12 +155,12 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
       return ORACLE_EINVAL;
   }
 #ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();  /* this call only */
 #else
   (void)nthreads;
 #endif
   int status = ORACLE_OK;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
   {
     double* p = (double*)malloc(sizeof(double) * (size_t)S);
     if (!p) {
@@ -527,14 +527,14 @@ int oracle_attn_rows_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         rows[3 * r + 2] < 0 || rows[3 * r + 2] >= S_q)
       return ORACLE_EINVAL;
 #ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();  /* this call only */
 #else
   (void)nthreads;
 #endif
   const int G = H / H_kv;
   const double sc = (double)scale;
   int status = ORACLE_OK;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
   {
     double* s = (double*)malloc(sizeof(double) * (size_t)S_kv);
     if (!s) {

@@ -566,3 +566,15 @@ def test_attn_rows_ex_closed_forms():
     for h in range(H):
         ref = oracle.attn_rows(q[:, :, h:h + 1].contiguous(), k1, v1, SCALE)
         assert np.max(np.abs(got[:, :, h:h + 1] - ref)) < 1e-12
+
+
+def test_thread_count_of_one_call_does_not_stick():
+    # a one-thread call must leave later calls on the default team size
+    before = oracle.num_threads()
+    q, k, v = rand_qkv(1, 64, 2, seed=41)
+    rows = np.array([[0, 0, 5], [0, 1, 63]], dtype=np.int64)
+    a = oracle.attn_rows(q, k, v, SCALE, rows=rows, nthreads=1)
+    b = oracle.attn_rows_ex(q, k, v, SCALE, (-1, 0), rows=rows, nthreads=1)
+    assert oracle.num_threads() == before
+    assert np.array_equal(a, oracle.attn_rows(q, k, v, SCALE, rows=rows))
+    assert np.array_equal(b, oracle.attn_rows_ex(q, k, v, SCALE, (-1, 0), rows=rows))
