@@ -22,6 +22,7 @@ headline's are drawn on the GPU from a seeded generator (same distribution).
     python bench.py [--steps K] [--warmup W] [--no-cpu] [--rows all|none|W:M,...]
     python bench.py --only wan720p:bf16,wan720p:sage_core --reps 3   # profiling runs
     python bench.py --copy-calibration     # plain copy for PMC byte scaling
+    python bench.py --ceilings             # library GEMM and copy rates (practical ceilings)
 """
 import argparse
 import hashlib
@@ -143,6 +144,59 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
+def ceilings(seconds=2.0, n=8192):
+    """Sustained throughput of plain library work on this board: hipBLASLt GEMMs through
+    torch (BF16 matmul, FP8 e4m3 _scaled_mm, INT8 _int_mm, n x n x n) and a 1 GiB device
+    copy, each run back to back for `seconds`.  These are the practical MFMA and HBM
+    ceilings under the board's power limit, next to which the kernels' fractions of the
+    published peaks are read."""
+    import torch
+    dev = torch.device("cuda")
+
+    def sustain(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps, t0 = 0, time.perf_counter()
+        e0.record()
+        while True:
+            for _ in range(10):
+                fn()
+            reps += 10
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 > seconds:
+                break
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {"seconds_each": seconds, "gemm_n": n}
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    ms = sustain(lambda: a @ b)
+    out["bf16_gemm_tflops"] = 2.0 * n ** 3 / ms / 1e9
+    del a, b
+    a8 = torch.randn(n, n, device=dev).to(torch.float8_e4m3fn)
+    b8 = torch.randn(n, n, device=dev).to(torch.float8_e4m3fn).t()
+    one = torch.ones((), device=dev)
+    ms = sustain(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+    out["fp8_gemm_tflops"] = 2.0 * n ** 3 / ms / 1e9
+    del a8, b8
+    ai = torch.randint(-127, 128, (n, n), device=dev, dtype=torch.int8)
+    bi = torch.randint(-127, 128, (n, n), device=dev, dtype=torch.int8)
+    ms = sustain(lambda: torch._int_mm(ai, bi))
+    out["int8_gemm_tops"] = 2.0 * n ** 3 / ms / 1e9
+    del ai, bi
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = sustain(lambda: dst.copy_(src))
+    out["copy_gbs"] = 2.0 * (1 << 30) / ms / 1e6  # bytes read + written
+    out["peaks"] = {"bf16_tflops": PEAK_TFLOPS["bf16"], "fp8_int8_tflops": PEAK_TFLOPS["fp8"],
+                    "hbm_gbs": PEAK_HBM_GBS}
+    print(json.dumps(out), flush=True)
+
+
 class Inputs:
     """Device inputs and output buffers of one workload, made once."""
 
@@ -226,6 +280,8 @@ def main():
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="sustained library GEMM and copy rates (the practical ceilings)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -240,6 +296,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ceilings:
+        ceilings()
         return
 
     ia.load()
