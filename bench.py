@@ -2,12 +2,14 @@
 
 Headline: the BF16 path at the FLUX-1024^2 shape (B=1, H=24, S=4608, D=128),
 attention TFLOPS = 4 * B * H * S^2 * D / time, inputs resident in HBM.  A step
-is one attn_fwd_bf16 call.  W warm-up steps, then exactly K timed steps, timed
+is one BF16 attention call (attn_fwd_bf16_ws, which at this shape runs the plain
+attn_fwd_bf16 kernel).  W warm-up steps, then exactly K timed steps, timed
 with HIP events recorded on the stream the kernel is launched on; events at the
 quarter marks give the first- and last-quarter ms per step (the clock regime).
 
 The same JSON line carries one row per (workload, mode) for the DiT shapes:
-  bf16       attn_fwd_bf16                      vs the BF16 MFMA peak
+  bf16       attn_fwd_bf16_ws (the plain attn_fwd_bf16 kernel unless the last round of
+             query tiles is split)                vs the BF16 MFMA peak
   sage       sage_prepare + sage_attn_fwd       vs the 8-bit MFMA peak
   sage_core  sage_attn_fwd on prepared tensors  vs the 8-bit MFMA peak
   prepare    sage_prepare                       vs the HBM peak (algorithmic bytes)
@@ -209,6 +211,11 @@ class Inputs:
         self.q, self.k, self.v = (t.to(dev) for t in qkv)
         self.out = torch.empty_like(self.q)
         self._prep = None
+        import image_dit_amd as ia
+        # the BF16 rows run attn_fwd_bf16_ws: the last, partial round of query tiles is split over
+        # every CU where that pays (workspace size > 0), else it is the plain attn_fwd_bf16 kernel
+        self.ws_bytes = ia.bf16_workspace_size(w.B, w.S, w.S, w.H, w.H)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev) if self.ws_bytes else None
 
     def prepared(self, stream):
         import image_dit_amd as ia
@@ -221,7 +228,8 @@ def mode_fn(inp, mode, stream):
     import image_dit_amd as ia
     w = inp.w
     if mode == "bf16":
-        return lambda: ia.attn_fwd_bf16(inp.q, inp.k, inp.v, w.scale, out=inp.out, stream=stream)
+        return lambda: ia.attn_fwd_bf16_ws(inp.q, inp.k, inp.v, w.scale, out=inp.out, workspace=inp.ws,
+                                           stream=stream)
     prep = inp.prepared(stream)
     if mode == "prepare":
         return lambda: ia.sage_prepare(inp.q, inp.k, inp.v, w.scale, out=prep, stream=stream)

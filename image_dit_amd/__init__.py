@@ -20,7 +20,8 @@ import os
 __all__ = ["DitAttnError", "load", "abi_version", "sage_padded_len", "sage_workspace_size",
            "attn_fwd_bf16", "attn_fwd_bf16_ex", "sage_prepare", "sage_prepare_ex",
            "qk_norm_rope_bf16", "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attention",
-           "sage_attention_ex", "sage_prepare_ex_noalloc", "STATIC_SCRATCH_BYTES", "HEAD_DIM", "LIB_PATH"]
+           "sage_attention_ex", "sage_prepare_ex_noalloc", "attn_fwd_bf16_ws", "bf16_workspace_size",
+           "STATIC_SCRATCH_BYTES", "HEAD_DIM", "LIB_PATH"]
 
 HEAD_DIM = 128
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
@@ -58,12 +59,15 @@ def load(path=None):
     lib.qk_norm_rope_bf16.argtypes = [vp, vp, ci, ci, ci, ci, vp, cf, vp, vp, ci, vp]
     lib.attn_fwd_bf16_ex.argtypes = [vp, vp, vp, vp] + [ci] * 6 + [cf, ci, ci, vp]
     lib.sage_prepare_ex_noalloc.argtypes = [vp] * 9 + [ci] * 6 + [cf, vp, vp, cf, vp, vp, ci, vp, vp]
+    lib.attn_fwd_bf16_ws.argtypes = [vp, vp, vp, vp] + [ci] * 6 + [cf, ci, ci, vp, ctypes.c_size_t, vp]
+    lib.ditattn_bf16_workspace_size.argtypes = [ci] * 7
+    lib.ditattn_bf16_workspace_size.restype = ctypes.c_size_t
     lib.sage_attn_fwd_ex.argtypes = [vp] * 7 + [ci] * 6 + [cf, ci, ci, vp]
     lib.ditattn_sage_workspace_size.argtypes = [ci, ci, ci]
     lib.ditattn_sage_workspace_size.restype = ctypes.c_size_t
     for name in ("attn_fwd_bf16", "sage_prepare", "sage_attn_fwd", "sage_prepare_ex",
                  "qk_norm_rope_bf16", "attn_fwd_bf16_ex", "sage_attn_fwd_ex",
-                 "sage_prepare_ex_noalloc"):
+                 "sage_prepare_ex_noalloc", "attn_fwd_bf16_ws"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -199,6 +203,48 @@ def attn_fwd_bf16_ex(q, k, v, scale, window=(-1, -1), out=None, stream=None):
     st = lib.attn_fwd_bf16_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv, H, H_kv, D,
                               float(scale), int(window[0]), int(window[1]), _stream_handle(stream))
     _status(lib, "attn_fwd_bf16_ex", st)
+    return out
+
+
+def bf16_workspace_size(B, S_q, S_kv, H, H_kv, window=(-1, -1)):
+    """Bytes of workspace attn_fwd_bf16_ws needs on the current device (0: no split)."""
+    return int(load().ditattn_bf16_workspace_size(int(B), int(S_q), int(S_kv), int(H), int(H_kv),
+                                                   int(window[0]), int(window[1])))
+
+
+def attn_fwd_bf16_ws(q, k, v, scale, window=(-1, -1), out=None, workspace=None, stream=None):
+    """attn_fwd_bf16_ex with a workspace that splits the last, partial round of query
+    tiles over every compute unit (see bf16_workspace_size).  workspace: a contiguous
+    device buffer of at least that many bytes, allocated (zero-filled) here when None.
+    One workspace serves one call at a time."""
+    import torch
+    lib = load()
+    B, S_q, H, D = _dims(q)
+    _, S_kv, H_kv, _ = _dims(k)
+    _check_bshd("q", q, torch.bfloat16)
+    for name, t in (("k", k), ("v", v)):
+        _check_bshd(name, t, torch.bfloat16)
+        if tuple(t.shape) != (B, S_kv, H_kv, D):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S_kv, H_kv, D)))
+    if out is None:
+        out = torch.empty_like(q)
+        _on_stream([out], stream)
+    else:
+        _check_out("out", out, (B, S_q, H, D), torch.bfloat16, q.device)
+    need = bf16_workspace_size(B, S_q, S_kv, H, H_kv, window)
+    ws_bytes = 0
+    if need:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+            _on_stream([workspace], stream)
+        elif (not workspace.is_cuda or not workspace.is_contiguous()
+              or workspace.numel() * workspace.element_size() < need):
+            raise ValueError("workspace must be a contiguous device buffer of >= %d bytes" % need)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd_bf16_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv, H, H_kv, D,
+                              float(scale), int(window[0]), int(window[1]),
+                              _ptr(workspace) if need else None, ws_bytes, _stream_handle(stream))
+    _status(lib, "attn_fwd_bf16_ws", st)
     return out
 
 

@@ -73,6 +73,15 @@ int check_xform(const void* norm_w0, const void* norm_w1, float eps, const void*
 
 float log2e_scale(float scale) { return static_cast<float>(static_cast<double>(scale) * kLog2eD); }
 
+// Per-call token of the split-tail flags: a flag counts as raised only when it holds this
+// call's value, so the workspace needs no clearing between calls.
+std::atomic<uint32_t> g_epoch{0};
+uint32_t next_epoch() {
+  uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
+
 // Device address of `scratch` on the current device, looked up on the first call on each
 // device and kept (the lookup allocates nothing; concurrent first calls store the same value).
 constexpr int kMaxDevices = 64;
@@ -143,6 +152,48 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o, int B
     return DITATTN_EINVAL;
   ditattn::Bf16Args a{q, k, v, o, B, S_q, S_kv, H, H_kv, log2e_scale(scale), window_left,
                       window_right, 0, 0, 0};
+  if (ditattn::launch_attn_fwd_bf16(a, stream) != hipSuccess) return DITATTN_EHIP;
+  return DITATTN_OK;
+}
+
+size_t ditattn_bf16_workspace_size(int B, int S_q, int S_kv, int H, int H_kv, int window_left,
+                                   int window_right) {
+  if (check_sizes(B, S_q, S_kv, H, H_kv, 128, 1.0f) != DITATTN_OK) return 0;
+  return ditattn::bf16_split_plan(B, S_q, S_kv, H, window_left, window_right).bytes;
+}
+
+int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int B, int S_q,
+                     int S_kv, int H, int H_kv, int D, float scale, int window_left,
+                     int window_right, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  int st = check_sizes(B, S_q, S_kv, H, H_kv, D, scale);
+  if (st != DITATTN_OK) return st;
+  if (window_left < -1 || window_right < -1) return DITATTN_EINVAL;
+  if (!q || !k || !v || !o) return DITATTN_EINVAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return DITATTN_EALIGN;
+  const int64_t q_bytes = static_cast<int64_t>(B) * S_q * H * 256;
+  const int64_t kv_bytes = static_cast<int64_t>(B) * S_kv * H_kv * 256;
+  if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) ||
+      overlaps(o, q_bytes, v, kv_bytes))
+    return DITATTN_EINVAL;
+  ditattn::Bf16Args a{q, k, v, o, B, S_q, S_kv, H, H_kv, log2e_scale(scale), window_left,
+                      window_right, 0, 0, 0};
+  const ditattn::Bf16Split plan = ditattn::bf16_split_plan(B, S_q, S_kv, H, window_left, window_right);
+  if (plan.grid > 0) {
+    if (!workspace || workspace_bytes < plan.bytes) return DITATTN_EINVAL;
+    if (misaligned(workspace)) return DITATTN_EALIGN;
+    const int64_t wb = static_cast<int64_t>(plan.bytes);
+    if (overlaps(workspace, wb, q, q_bytes) || overlaps(workspace, wb, k, kv_bytes) ||
+        overlaps(workspace, wb, v, kv_bytes) || overlaps(workspace, wb, o, q_bytes))
+      return DITATTN_EINVAL;
+    a.sk_grid = plan.grid;
+    a.sk_rounds = plan.rounds;
+    a.sk_nk = plan.nk;
+    a.sk_tail_units = plan.tail_units;
+    a.ws_flag = static_cast<uint32_t*>(workspace);
+    a.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.flag_bytes);
+    a.epoch = next_epoch();
+  }
   if (ditattn::launch_attn_fwd_bf16(a, stream) != hipSuccess) return DITATTN_EHIP;
   return DITATTN_OK;
 }

@@ -219,6 +219,36 @@ int sage_prepare_ex_noalloc(const void* q, const void* k, const void* v, int8_t*
                             float norm_eps, const void* rope_cos, const void* rope_sin,
                             int rope_dim, float* k_mean, hipStream_t stream);
 
+/*
+ * attn_fwd_bf16_ws -- attn_fwd_bf16_ex with a workspace that lets the last, partial
+ * round of query tiles be split over every compute unit.  Same operation ("Kernel
+ * acceleration: attention, compilation and fusion", section "Attention: from O(N^2)
+ * memory to blocks": the blocked form with running max and sum), same arguments,
+ * checks and status codes as attn_fwd_bf16_ex, plus:
+ *   workspace        device pointer, 16-byte aligned, overlapping no tensor, at least
+ *                    ditattn_bf16_workspace_size(...) bytes (owned by the caller;
+ *                    zero-filled once before first use is recommended); may be NULL
+ *                    when that size is 0
+ *   workspace_bytes  its size; too small -> DITATTN_EINVAL before anything is enqueued
+ * When the size is 0 (key window on, fewer query tiles than compute units, or a last
+ * round that already fills the GPU) the call is attn_fwd_bf16_ex.  Otherwise the grid is
+ * one workgroup per compute unit: whole query tiles first, then equal ranges of (query
+ * tile, key tile) units; a query tile split over several workgroups is merged, in a
+ * fixed order, by the one holding its last key tile from FP32 partials (m, l, O) the
+ * others leave in the workspace.  The result meets the same accuracy as attn_fwd_bf16_ex's
+ * (it differs from it by the rounding of P to BF16, taken relative to each piece's own
+ * running max) and is run-to-run deterministic.  One workspace serves one call at a time.
+ */
+int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int B, int S_q,
+                     int S_kv, int H, int H_kv, int D, float scale, int window_left,
+                     int window_right, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Workspace bytes attn_fwd_bf16_ws needs on the current device (0: no split; also 0 for
+ * sizes the library rejects). */
+size_t ditattn_bf16_workspace_size(int B, int S_q, int S_kv, int H, int H_kv, int window_left,
+                                   int window_right);
+
 /* Workspace bytes sage_prepare_ex needs for K smoothing at these sizes (0 for
  * sizes it rejects).  Touches no GPU. */
 size_t ditattn_sage_workspace_size(int B, int S_kv, int H_kv);

@@ -317,3 +317,20 @@ def test_noalloc_rejects_before_any_hip_call(lib):
     # argument errors come first, as in sage_prepare_ex
     assert call(H=3, H_kv=2, k_mean=W) == EINVAL
     assert call(H=3, H_kv=2) == EINVAL
+
+
+# ---------------------------------------------------------------- attn_fwd_bf16_ws
+def test_bf16_ws_rejects_before_any_hip_call(lib):
+    vp = ctypes.c_void_p
+
+    def call(B=1, S=64, H=2, D=128, wl=-1, wr=-1, o=GOOD * 2 ** 22):
+        return lib.attn_fwd_bf16_ws(vp(GOOD), vp(GOOD * 2 ** 20), vp(GOOD * 2 ** 21), vp(o), B, S, S, H, H,
+                                    D, ctypes.c_float(0.088), wl, wr, None, 0, None)
+    assert call(D=64) == EUNSUPPORTED
+    assert call(wl=-2) == EINVAL
+    assert call(o=GOOD * 2 ** 22 + 2) == EALIGN
+    assert call(o=GOOD) == EINVAL  # output over q
+    assert call(H=MAX_HEADS + 1) == EOVERFLOW
+    # without a GPU the plan is "no split", so the size is 0 and no workspace is needed
+    assert lib.ditattn_bf16_workspace_size(1, 4608, 4608, 24, 24, -1, -1) == 0
+    assert lib.ditattn_bf16_workspace_size(1, 0, 4608, 24, 24, -1, -1) == 0
