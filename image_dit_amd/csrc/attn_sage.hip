@@ -20,9 +20,16 @@
 //     an order that gives each half-wave 32 consecutive keys, i.e. one 32-row K
 //     block and one k_scale: a lane's scores are x = acc * s with
 //     s = q_scale * k_scale, already in base-2 units.  The accumulators start
-//     at the bit pattern of 1.5 * 2^23, so an int32 sum read as fp32 is exactly
-//     1.5 * 2^23 + score: the row max is taken on those bit patterns and
-//     p = exp2(score * s - m + 8) is one FMA and one exp2, no conversion.
+//     at the bit pattern of 1/(2 pi) (an inline constant), so an int32 sum read
+//     as fp32 is exactly 1/(2 pi) + score * 2^-26: the row max is taken on those
+//     bit patterns and p = exp2(score * s - m + 8) is one FMA and one exp2, no
+//     conversion.
+//   * Matrix phase reads are issued as explicit LDS instructions ahead of the
+//     MFMAs that take them: four K fragments, the tile's k_scale pair and two
+//     V^T fragments at the start of the phase, then one K fragment (later two
+//     V^T fragments) after each MFMA.  Each MFMA waits only for its own operands
+//     (LDS reads return in issue order), so the phase pays about one LDS latency
+//     instead of one per fragment, as the compiler's own placement did.
 //   * P V on v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 operands, unit block
 //     scales): A = V^T tile (channels x 64 keys) from LDS, B = P from registers
 //     (the S^T accumulator of a lane already holds the B operand's keys).
@@ -62,7 +69,13 @@ constexpr float kPScaleLog2 = 8.0f;  // P is stored as p * 2^8
 // The running max is raised only when a row's tile max exceeds it by more than
 // this (base-2 units).  P then stays <= 2^0.8, so p * 2^8 <= 445.7 fits e4m3.
 constexpr float kLazyThresh = 0.8f;
-constexpr float kSeed = 12582912.0f;  // 1.5 * 2^23, the fp32 value of the accumulator seed 0x4B400000
+// K Q^T accumulator seed: the bit pattern of 1/(2 pi) (0x3E22F983), an inline constant of the
+// MFMA's accumulator operand, so the seed takes no registers.  Its mantissa field, 2293123,
+// stays inside [0, 2^23) after adding any score (|score| <= 128 * 127^2 = 2064512): the int32
+// sum read as fp32 is exactly kSeed + score * 2^-26.
+constexpr uint32_t kSeedBits = 0x3E22F983u;
+constexpr float kSeed = __builtin_bit_cast(float, kSeedBits);
+constexpr float kScoreUnit = 0x1p26f;  // a seeded score moves in steps of 2^-26
 
 // LDS tiles (bytes):  K: 64 key rows x 128 B, 16-B chunk c of row r stored at c ^ ((r >> 1) & 7).
 //                     V^T: 128 channel rows x 64 B, chunk c of row r at c ^ ((r >> 2) & 3).
@@ -177,15 +190,14 @@ sage_attn_fwd_kernel(SageArgs a) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) vofs[c2] = ln * 64 + 16 * ((2 * hl + c2) ^ ((ln >> 2) & 3));
 
-    // The K Q^T accumulators start at the bit pattern of 1.5 * 2^23 (0x4B400000): with
-    // |score| < 2^21 the int32 sum read as fp32 is then exactly 1.5 * 2^23 + score, so the
+    // The K Q^T accumulators start at kSeedBits (an inline constant of the MFMA), so the
     // scores need no int -> fp32 conversion (see the softmax).
     i32x16 seed;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) seed[r] = 0x4B400000;
+    for (int r = 0; r < 16; ++r) seed[r] = (int)kSeedBits;
     i32x16 si[2];  // biased int32 scores of the latest tile, one 32-key sub-tile each
     i32x8 pf;      // P of the latest softmax (e4m3, p * 2^8)
-    float s_tile;  // q_scale * k_scale of the half-wave's 32-key block in that tile
+    float s_tile;  // q_scale * k_scale * 2^26 of the half-wave's 32-key block in that tile
     // ---- matrix phase: O^T += V^T P^T (and the row sums) for V stage VS (4 + 1 MFMA) and/or
     // S^T = K Q^T for K stage KS (8 MFMA).
     float mx_tile;  // row max (scaled, log2 units) of the latest K Q^T, -inf where all hidden
@@ -196,29 +208,76 @@ sage_attn_fwd_kernel(SageArgs a) {
     auto mphase = [&](auto vs_c, auto ks_c, auto pv_c, auto qk_c, int t) __attribute__((always_inline)) {
       constexpr int VS = decltype(vs_c)::value, KS = decltype(ks_c)::value;
       constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
-      const DITATTN_LDS char* kb = (const DITATTN_LDS char*)(lds + K_STAGE0 + KS * KT_BYTES);
-      const DITATTN_LDS char* vb = (const DITATTN_LDS char*)(lds + V_STAGE0 + VS * VT_BYTES);
+      constexpr int KB = K_STAGE0 + KS * KT_BYTES, VB = V_STAGE0 + VS * VT_BYTES, SB = KS_STAGE0 + KS * 16;
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(const DITATTN_LDS char*)lds;
+      // Fragment reads: K fragment j = 2 ks + tt (sub-tile tt adds 16 rows = 2 KB), the tile's
+      // k_scale pair (read with the K rows: the stage is refilled one window later, while the
+      // other group may still be in this tile's softmax), V^T fragment j = 2 dt + c2 (dt adds
+      // 32 channel rows = 2 KB).  Four K fragments are in flight ahead of the MFMA that takes
+      // them and the V^T reads follow as the K registers free up; each MFMA waits only for its
+      // own operands (LDS reads return in issue order), so the phase pays about one LDS latency.
+      u32x4 kf[8], vf[8];
+      uint32_t ksb = 0;
+      auto kread = [&](auto j_c) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_c)::value;
+        kf[j] = ds_read_b128<KB + (j & 1) * 2048>(lds0 + kofs[j >> 1]);
+      };
+      auto vread = [&](auto j_c) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_c)::value;
+        vf[j] = ds_read_b128<VB + (j >> 1) * 2048>(lds0 + vofs[j & 1]);
+      };
+      using J0 = std::integral_constant<int, 0>;
+      using J1 = std::integral_constant<int, 1>;
+      using J2 = std::integral_constant<int, 2>;
+      using J3 = std::integral_constant<int, 3>;
+      using J4 = std::integral_constant<int, 4>;
+      using J5 = std::integral_constant<int, 5>;
+      using J6 = std::integral_constant<int, 6>;
+      using J7 = std::integral_constant<int, 7>;
+      // Issue order with both parts: K0 K1 K2 K3 S V0 V1, then after MFMA j: K(j+4) (j < 4),
+      // V2 V3 (j = 4), V4 V5 (j = 5), V6 V7 (j = 6).  Without P V: K0..K3 S, then K(j+4).
+      // Position of each read in that order, and the reads issued before the wait for K j:
+      constexpr int kpos_pv[8] = {0, 1, 2, 3, 7, 8, 9, 10}, kpos_qk[8] = {0, 1, 2, 3, 5, 6, 7, 8};
+      constexpr int before_pv[8] = {7, 8, 9, 10, 11, 13, 15, 17}, before_qk[8] = {5, 6, 7, 8, 9, 9, 9, 9};
+      constexpr int vpos[8] = {5, 6, 11, 12, 13, 14, 15, 16};
       if constexpr (QK) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const i32x4 kf = *(const DITATTN_LDS i32x4*)(kb + kofs[ks] + tt * 16 * 128);
-            si[tt] = mfma_i8_32x32x32(kf, qf[ks], ks == 0 ? seed : si[tt]);
-          }
+        kread(J0{}); kread(J1{}); kread(J2{}); kread(J3{});
+        ksb = ds_read_b32<SB>(lds0 + 4 * hl);
+        if constexpr (PV) {
+          vread(J0{}); vread(J1{});
         }
-        // read with the K rows: the stage is refilled one window later, while the
-        // other group may still be in this tile's softmax
-        s_tile = sq * *(const DITATTN_LDS float*)(lds + KS_STAGE0 + KS * 16 + 4 * hl);
+        auto qk = [&](auto j_c) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_c)::value;
+          constexpr int later = PV ? before_pv[j] - kpos_pv[j] - 1 : before_qk[j] - kpos_qk[j] - 1;
+          lds_wait<later>(kf[j]);
+          si[j & 1] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, kf[j]), qf[j >> 1], j < 2 ? seed : si[j & 1]);
+          if constexpr (j < 4) {
+            kread(std::integral_constant<int, j + 4>{});
+          } else if constexpr (PV) {
+            if constexpr (j == 4) { vread(J2{}); vread(J3{}); }
+            if constexpr (j == 5) { vread(J4{}); vread(J5{}); }
+            if constexpr (j == 6) { vread(J6{}); vread(J7{}); }
+          }
+          // keep each MFMA between its wait and the next one
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        qk(J0{}); qk(J1{}); qk(J2{}); qk(J3{}); qk(J4{}); qk(J5{}); qk(J6{}); qk(J7{});
+        lds_wait<PV ? 17 - 4 - 1 : 9 - 4 - 1>(ksb);
+        s_tile = sq * __uint_as_float(ksb) * kScoreUnit;
+      } else if constexpr (PV) {
+        vread(J0{}); vread(J1{}); vread(J2{}); vread(J3{}); vread(J4{}); vread(J5{}); vread(J6{}); vread(J7{});
       }
       if constexpr (PV) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const i32x4 v0 = *(const DITATTN_LDS i32x4*)(vb + vofs[0] + dt * 32 * 64);
-          const i32x4 v1 = *(const DITATTN_LDS i32x4*)(vb + vofs[1] + dt * 32 * 64);
-          const i32x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        auto pv = [&](auto dt_c) __attribute__((always_inline)) {
+          constexpr int dt = decltype(dt_c)::value;
+          constexpr int later = QK ? 17 - vpos[2 * dt + 1] - 1 : 6 - 2 * dt;
+          lds_wait<later>(vf[2 * dt], vf[2 * dt + 1]);
+          const i32x8 va = __builtin_shufflevector(__builtin_bit_cast(i32x4, vf[2 * dt]),
+                                                   __builtin_bit_cast(i32x4, vf[2 * dt + 1]), 0, 1, 2, 3, 4, 5, 6, 7);
           acc[dt] = mfma_fp8_32x32x64(va, pf, acc[dt], unit_scale);
-        }
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        pv(J0{}); pv(J1{}); pv(J2{}); pv(J3{});
         lacc = mfma_fp8_32x32x64(ones, pf, lacc, unit_scale);
       }
       if constexpr (QK) {
@@ -275,9 +334,10 @@ sage_attn_fwd_kernel(SageArgs a) {
         lacc *= alpha;
       }
       const float mneg = m == -INFINITY ? 0.0f : kPScaleLog2 - m;  // rows with no visible key yet
-      // x = score * s - m + 8 as ONE fma on the biased pattern A = 1.5 * 2^23 + score:
-      // A * s + (mneg - 1.5 * 2^23 * s).  The constant's rounding error is below 0.75 s, i.e.
-      // under one unit of the int32 dot product (whose INT8 quantization noise is far larger).
+      // x = score * q_scale * k_scale - m + 8 as ONE fma on the seeded pattern
+      // A = kSeed + score * 2^-26 with s = q_scale * k_scale * 2^26: A * s + (mneg - kSeed * s).
+      // The constant's rounding error is below q_scale * k_scale / 2, i.e. under half a unit
+      // of the int32 dot product (whose INT8 quantization noise is far larger).
       const float cst = fmaf(-kSeed, s, mneg);
       float p[32];
 #pragma unroll
@@ -293,7 +353,8 @@ sage_attn_fwd_kernel(SageArgs a) {
       // P (B operand, 32 e4m3 bytes): byte e = key 32 hl + e
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], 0, false);
+        // the low half is written here and the high half below: the old word's bits are discarded
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], pf[w], false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
         pf[w] = word;
       }

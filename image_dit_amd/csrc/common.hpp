@@ -84,6 +84,24 @@ __device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET) : "memory");
   return r;
 }
+// ds_read_b32 as inline assembly (see above); `addr` is an LDS byte address.
+template <int OFFSET>
+__device__ __forceinline__ uint32_t ds_read_b32(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFFSET) : "memory");
+  return r;
+}
+// Wait until at most N LDS operations are outstanding; x depends on the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4& x) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(uint32_t& x) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
 // Wait until at most N LDS operations are outstanding; a and b depend on the wait.
 template <int N>
 __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
