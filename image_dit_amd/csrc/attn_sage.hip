@@ -20,7 +20,7 @@
 //     an order that gives each half-wave 32 consecutive keys, i.e. one 32-row K
 //     block and one k_scale: a lane's scores are x = acc * s with
 //     s = q_scale * k_scale, already in base-2 units.  The accumulators start
-//     at the bit pattern of 1/(2 pi) (an inline constant), so an int32 sum read
+//     at the bit pattern of 1/(2 pi), so an int32 sum read
 //     as fp32 is exactly 1/(2 pi) + score * 2^-26: the row max is taken on those
 //     bit patterns and p = exp2(score * s - m + 8) is one FMA and one exp2, no
 //     conversion.
@@ -69,8 +69,7 @@ constexpr float kPScaleLog2 = 8.0f;  // P is stored as p * 2^8
 // The running max is raised only when a row's tile max exceeds it by more than
 // this (base-2 units).  P then stays <= 2^0.8, so p * 2^8 <= 445.7 fits e4m3.
 constexpr float kLazyThresh = 0.8f;
-// K Q^T accumulator seed: the bit pattern of 1/(2 pi) (0x3E22F983), an inline constant of the
-// MFMA's accumulator operand, so the seed takes no registers.  Its mantissa field, 2293123,
+// K Q^T accumulator seed: the bit pattern of 1/(2 pi) (0x3E22F983).  Its mantissa field, 2293123,
 // stays inside [0, 2^23) after adding any score (|score| <= 128 * 127^2 = 2064512): the int32
 // sum read as fp32 is exactly kSeed + score * 2^-26.
 constexpr uint32_t kSeedBits = 0x3E22F983u;
@@ -151,8 +150,9 @@ sage_attn_fwd_kernel(SageArgs a) {
   lacc = f32x16{};
   float m = -INFINITY;
   const int unit_scale = unit_e8m0_scale();
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  asm volatile("" : "+v"(ones));  // kept in registers (else rebuilt before every row-sum MFMA)
 
   if (n > 0) {
     // ---- global -> LDS (direct); every lane fetches the chunk that lands in its LDS slot.
@@ -190,11 +190,14 @@ sage_attn_fwd_kernel(SageArgs a) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) vofs[c2] = ln * 64 + 16 * ((2 * hl + c2) ^ ((ln >> 2) & 3));
 
-    // The K Q^T accumulators start at kSeedBits (an inline constant of the MFMA), so the
-    // scores need no int -> fp32 conversion (see the softmax).
+    // The K Q^T accumulators start at kSeedBits, so the scores need no int -> fp32
+    // conversion (see the softmax).
     i32x16 seed;
 #pragma unroll
     for (int r = 0; r < 16; ++r) seed[r] = (int)kSeedBits;
+    // Kept in registers for the whole loop: left as a constant, the compiler rebuilds it from
+    // scalar registers before every tile's first MFMAs (eight 64-bit moves per tile).
+    asm volatile("" : "+v"(seed));
     i32x16 si[2];  // biased int32 scores of the latest tile, one 32-key sub-tile each
     i32x8 pf;      // P of the latest softmax (e4m3, p * 2^8)
     float s_tile;  // q_scale * k_scale * 2^26 of the half-wave's 32-key block in that tile
