@@ -90,6 +90,15 @@ constexpr int KS_STAGE0 = NSTAGE * (KT_BYTES + VT_BYTES);  // the tile's two k_s
 // 32 FP8 bytes of a lane are 32 consecutive keys and V^T is read with two 16-byte loads.
 __device__ __forceinline__ int key_of_row(int m, int tt) { return 32 * ((m >> 2) & 1) + 16 * tt + 4 * (m >> 3) + (m & 3); }
 
+// half_pair_max for values that are never NaN: one v_max_f32, without the canonicalizing
+// moves fmaxf adds.
+__device__ __forceinline__ float half_pair_max_nc(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float y;
+  asm("v_max_f32 %0, %1, %2" : "=v"(y) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  return y;
+}
+
 // First and last key query row i sees (an empty range when hi < lo).
 __device__ __forceinline__ int key_lo(const SageArgs& a, int i) {
   if (a.wl < 0) return 0;
@@ -128,7 +137,8 @@ sage_attn_fwd_kernel(SageArgs a) {
   i32x4 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const i32x4*)(qbh + (int64_t)qi * kHeadDim + 32 * ks + 16 * hl);
-  const float sq = a.q_scale[(int64_t)bh * nblk_q + q0 / 32];
+  // q_scale * 2^26: s_tile below is then one product (the power of two is exact)
+  const float sq = a.q_scale[(int64_t)bh * nblk_q + q0 / 32] * kScoreUnit;
 
   // ---- key range.  Query i sees keys j with lo(i) <= j <= hi(i): lo = i + off - wl (wl >= 0),
   // hi = i + off + wr (wr >= 0), off = S_kv - S_q, both clamped to [0, S_kv - 1] (computed in
@@ -149,6 +159,9 @@ sage_attn_fwd_kernel(SageArgs a) {
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
   lacc = f32x16{};
   float m = -INFINITY;
+  // Kept with m (which changes only when the running max is raised): m + kLazyThresh, and the
+  // exp2 offset 8 - m (0 while a row has no visible key, m = -inf).
+  float m_thr = -INFINITY, mneg = 0.0f;
   const int unit_scale = unit_e8m0_scale();
   i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                 0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
@@ -266,7 +279,7 @@ sage_attn_fwd_kernel(SageArgs a) {
         };
         qk(J0{}); qk(J1{}); qk(J2{}); qk(J3{}); qk(J4{}); qk(J5{}); qk(J6{}); qk(J7{});
         lds_wait<PV ? 17 - 4 - 1 : 9 - 4 - 1>(ksb);
-        s_tile = sq * __uint_as_float(ksb) * kScoreUnit;
+        s_tile = sq * __uint_as_float(ksb);
       } else if constexpr (PV) {
         vread(J0{}); vread(J1{}); vread(J2{}); vread(J3{}); vread(J4{}); vread(J5{}); vread(J6{}); vread(J7{});
       }
@@ -308,7 +321,7 @@ sage_attn_fwd_kernel(SageArgs a) {
                            max(max(max(m8[6], m8[7]), m8[8]), max(m8[9], m8[10])));
         // s >= 0: scaling keeps the max; a half-wave with every key hidden contributes -inf
         const float mh = mi == kMasked ? -INFINITY : (__int_as_float(mi) - kSeed) * s_tile;
-        mx_tile = half_pair_max(mh);
+        mx_tile = half_pair_max_nc(mh);
         pin(si[0]);
         pin(si[1]);
         pin(mx_tile);
@@ -328,15 +341,16 @@ sage_attn_fwd_kernel(SageArgs a) {
       const float s = s_tile;
       const bool masked = masked_tile(t);  // uniform
       const float mx = mx_tile;
-      if (__builtin_amdgcn_ballot_w64(mx > m + kLazyThresh) != 0) {
+      if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
         const float m_new = fmaxf(m, mx);
         const float alpha = m_new == m ? 1.0f : fast_exp2(m - m_new);
         m = m_new;
+        m_thr = m + kLazyThresh;
+        mneg = m == -INFINITY ? 0.0f : kPScaleLog2 - m;  // rows with no visible key yet
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
         lacc *= alpha;
       }
-      const float mneg = m == -INFINITY ? 0.0f : kPScaleLog2 - m;  // rows with no visible key yet
       // x = score * q_scale * k_scale - m + 8 as ONE fma on the seeded pattern
       // A = kSeed + score * 2^-26 with s = q_scale * k_scale * 2^26: A * s + (mneg - kSeed * s).
       // The constant's rounding error is below q_scale * k_scale / 2, i.e. under half a unit
