@@ -97,11 +97,25 @@ def sage_workspace_size(B, S_kv, H_kv):
     return int(load().ditattn_sage_workspace_size(int(B), int(S_kv), int(H_kv)))
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device=None):
+    """The HIP stream to launch on: `stream`, or the current stream of `device`.  A stream
+    of another device than the tensors' is refused (the kernels would run on the wrong GPU)."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
+    elif device is not None and stream.device != device:
+        raise ValueError("stream is on %s, the tensors on %s" % (stream.device, device))
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on_device(device):
+    """Make the tensors' GPU the current device for a library call: the library launches on
+    the current device and sizes the split-tail grid and the static scratch by it."""
+    import contextlib
+    import torch
+    if device is None or device.type != "cuda":
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
 
 
 def _on_stream(tensors, stream):
@@ -119,10 +133,12 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _check_bshd(name, t, dtype):
+def _check_bshd(name, t, dtype, device=None):
     import torch
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise TypeError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
@@ -155,6 +171,15 @@ def _prepared_specs(B, S, H, D, S_kv=None, H_kv=None):
             ("v_fp8", (B, H_kv, D, Sk), torch.uint8), ("v_scale", (B, H_kv, D), torch.float32))
 
 
+def _check_workspace(t, nbytes, device):
+    """A caller-supplied workspace: a contiguous tensor on the tensors' GPU, >= nbytes."""
+    import torch
+    if (not isinstance(t, torch.Tensor) or t.device != device or not t.is_contiguous()
+            or t.numel() * t.element_size() < nbytes):
+        raise ValueError("workspace must be a contiguous tensor on %s of >= %d bytes" % (device, nbytes))
+    return t.numel() * t.element_size()
+
+
 def _dims(q):
     if q.dim() != 4:
         raise ValueError("expected [B, S, H, D], got shape %s" % (tuple(q.shape),))
@@ -167,7 +192,7 @@ def attn_fwd_bf16(q, k, v, scale, out=None, stream=None):
     lib = load()
     B, S, H, D = _dims(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_bshd(name, t, torch.bfloat16)
+        _check_bshd(name, t, torch.bfloat16, device=q.device)
         if tuple(t.shape) != (B, S, H, D):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S, H, D)))
     if out is None:
@@ -175,8 +200,9 @@ def attn_fwd_bf16(q, k, v, scale, out=None, stream=None):
         _on_stream([out], stream)
     else:
         _check_out("out", out, (B, S, H, D), torch.bfloat16, q.device)
-    st = lib.attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, H, D, float(scale),
-                           _stream_handle(stream))
+    with _on_device(q.device):
+        st = lib.attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, H, D, float(scale),
+                               _stream_handle(stream, q.device))
     _status(lib, "attn_fwd_bf16", st)
     return out
 
@@ -192,7 +218,7 @@ def attn_fwd_bf16_ex(q, k, v, scale, window=(-1, -1), out=None, stream=None):
     _, S_kv, H_kv, _ = _dims(k)
     _check_bshd("q", q, torch.bfloat16)
     for name, t in (("k", k), ("v", v)):
-        _check_bshd(name, t, torch.bfloat16)
+        _check_bshd(name, t, torch.bfloat16, device=q.device)
         if tuple(t.shape) != (B, S_kv, H_kv, D):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S_kv, H_kv, D)))
     if out is None:
@@ -200,8 +226,10 @@ def attn_fwd_bf16_ex(q, k, v, scale, window=(-1, -1), out=None, stream=None):
         _on_stream([out], stream)
     else:
         _check_out("out", out, (B, S_q, H, D), torch.bfloat16, q.device)
-    st = lib.attn_fwd_bf16_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv, H, H_kv, D,
-                              float(scale), int(window[0]), int(window[1]), _stream_handle(stream))
+    with _on_device(q.device):
+        st = lib.attn_fwd_bf16_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv, H, H_kv, D,
+                                  float(scale), int(window[0]), int(window[1]),
+                                  _stream_handle(stream, q.device))
     _status(lib, "attn_fwd_bf16_ex", st)
     return out
 
@@ -223,7 +251,7 @@ def attn_fwd_bf16_ws(q, k, v, scale, window=(-1, -1), out=None, workspace=None, 
     _, S_kv, H_kv, _ = _dims(k)
     _check_bshd("q", q, torch.bfloat16)
     for name, t in (("k", k), ("v", v)):
-        _check_bshd(name, t, torch.bfloat16)
+        _check_bshd(name, t, torch.bfloat16, device=q.device)
         if tuple(t.shape) != (B, S_kv, H_kv, D):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S_kv, H_kv, D)))
     if out is None:
@@ -231,19 +259,19 @@ def attn_fwd_bf16_ws(q, k, v, scale, window=(-1, -1), out=None, workspace=None, 
         _on_stream([out], stream)
     else:
         _check_out("out", out, (B, S_q, H, D), torch.bfloat16, q.device)
-    need = bf16_workspace_size(B, S_q, S_kv, H, H_kv, window)
+    with _on_device(q.device):  # the split plan depends on the device's compute units
+        need = bf16_workspace_size(B, S_q, S_kv, H, H_kv, window)
     ws_bytes = 0
     if need:
         if workspace is None:
             workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
             _on_stream([workspace], stream)
-        elif (not workspace.is_cuda or not workspace.is_contiguous()
-              or workspace.numel() * workspace.element_size() < need):
-            raise ValueError("workspace must be a contiguous device buffer of >= %d bytes" % need)
-        ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.attn_fwd_bf16_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv, H, H_kv, D,
-                              float(scale), int(window[0]), int(window[1]),
-                              _ptr(workspace) if need else None, ws_bytes, _stream_handle(stream))
+        ws_bytes = _check_workspace(workspace, need, q.device)
+    with _on_device(q.device):
+        st = lib.attn_fwd_bf16_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv, H, H_kv, D,
+                                  float(scale), int(window[0]), int(window[1]),
+                                  _ptr(workspace) if need else None, ws_bytes,
+                                  _stream_handle(stream, q.device))
     _status(lib, "attn_fwd_bf16_ws", st)
     return out
 
@@ -259,7 +287,7 @@ def sage_prepare(q, k, v, scale, out=None, stream=None):
     lib = load()
     B, S, H, D = _dims(q)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_bshd(name, t, torch.bfloat16)
+        _check_bshd(name, t, torch.bfloat16, device=q.device)
         if tuple(t.shape) != (B, S, H, D):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S, H, D)))
     specs = _prepared_specs(B, S, H, D)
@@ -271,8 +299,9 @@ def sage_prepare(q, k, v, scale, out=None, stream=None):
             raise ValueError("out must be the 6 tensors of a sage_prepare result")
         for t, (name, shape, dt) in zip(out, specs):
             _check_out(name, t, shape, dt, q.device)
-    st = lib.sage_prepare(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S, H, D,
-                          float(scale), _stream_handle(stream))
+    with _on_device(q.device):
+        st = lib.sage_prepare(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S, H, D,
+                              float(scale), _stream_handle(stream, q.device))
     _status(lib, "sage_prepare", st)
     return out
 
@@ -300,7 +329,7 @@ def sage_prepare_ex(q, k, v, scale, q_norm_w=None, k_norm_w=None, norm_eps=1e-6,
     _, S_kv, H_kv, _ = _dims(k)
     _check_bshd("q", q, torch.bfloat16)
     for name, t in (("k", k), ("v", v)):
-        _check_bshd(name, t, torch.bfloat16)
+        _check_bshd(name, t, torch.bfloat16, device=q.device)
         if tuple(t.shape) != (B, S_kv, H_kv, D):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S_kv, H_kv, D)))
     dev = q.device
@@ -331,16 +360,15 @@ def sage_prepare_ex(q, k, v, scale, q_norm_w=None, k_norm_w=None, norm_eps=1e-6,
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
             _on_stream([workspace], stream)
-        elif workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous buffer of >= %d bytes" % ws_bytes)
-        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_bytes = _check_workspace(workspace, ws_bytes, dev)
     else:
         k_mean = workspace = None
-    st = lib.sage_prepare_ex(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S_q, S_kv, H,
-                             H_kv, D, float(scale), _opt_ptr(q_norm_w), _opt_ptr(k_norm_w),
-                             float(norm_eps), _opt_ptr(rope_cos if rope_dim else None),
-                             _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
-                             _opt_ptr(k_mean), _opt_ptr(workspace), ws_bytes, _stream_handle(stream))
+    with _on_device(dev):
+        st = lib.sage_prepare_ex(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S_q, S_kv, H,
+                                 H_kv, D, float(scale), _opt_ptr(q_norm_w), _opt_ptr(k_norm_w),
+                                 float(norm_eps), _opt_ptr(rope_cos if rope_dim else None),
+                                 _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
+                                 _opt_ptr(k_mean), _opt_ptr(workspace), ws_bytes, _stream_handle(stream, dev))
     _status(lib, "sage_prepare_ex", st)
     return tuple(out) + ((k_mean,) if smooth_k else ())
 
@@ -356,7 +384,7 @@ def sage_prepare_ex_noalloc(q, k, v, scale, out, k_mean=None, q_norm_w=None, k_n
     _, S_kv, H_kv, _ = _dims(k)
     _check_bshd("q", q, torch.bfloat16)
     for name, t in (("k", k), ("v", v)):
-        _check_bshd(name, t, torch.bfloat16)
+        _check_bshd(name, t, torch.bfloat16, device=q.device)
         if tuple(t.shape) != (B, S_kv, H_kv, D):
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, S_kv, H_kv, D)))
     dev = q.device
@@ -373,12 +401,13 @@ def sage_prepare_ex_noalloc(q, k, v, scale, out, k_mean=None, q_norm_w=None, k_n
     for t, (name, shape, dt) in zip(out, _prepared_specs(B, S_q, H, D, S_kv, H_kv)):
         _check_out(name, t, shape, dt, dev)
     _check_small("k_mean", k_mean, (B, H_kv, D), torch.float32, dev)
-    st = lib.sage_prepare_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S_q,
-                                     S_kv, H, H_kv, D, float(scale), _opt_ptr(q_norm_w),
-                                     _opt_ptr(k_norm_w), float(norm_eps),
-                                     _opt_ptr(rope_cos if rope_dim else None),
-                                     _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
-                                     _opt_ptr(k_mean), _stream_handle(stream))
+    with _on_device(dev):
+        st = lib.sage_prepare_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), *[_ptr(t) for t in out], B, S_q,
+                                         S_kv, H, H_kv, D, float(scale), _opt_ptr(q_norm_w),
+                                         _opt_ptr(k_norm_w), float(norm_eps),
+                                         _opt_ptr(rope_cos if rope_dim else None),
+                                         _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
+                                         _opt_ptr(k_mean), _stream_handle(stream, dev))
     _status(lib, "sage_prepare_ex_noalloc", st)
     return tuple(out) + ((k_mean,) if k_mean is not None else ())
 
@@ -403,10 +432,11 @@ def qk_norm_rope_bf16(x, norm_w=None, norm_eps=1e-6, rope_cos=None, rope_sin=Non
         _on_stream([out], stream)
     else:
         _check_out("out", out, (B, S, H, D), torch.bfloat16, dev)
-    st = lib.qk_norm_rope_bf16(_ptr(x), _ptr(out), B, S, H, D, _opt_ptr(norm_w), float(norm_eps),
-                               _opt_ptr(rope_cos if rope_dim else None),
-                               _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
-                               _stream_handle(stream))
+    with _on_device(dev):
+        st = lib.qk_norm_rope_bf16(_ptr(x), _ptr(out), B, S, H, D, _opt_ptr(norm_w), float(norm_eps),
+                                   _opt_ptr(rope_cos if rope_dim else None),
+                                   _opt_ptr(rope_sin if rope_dim else None), int(rope_dim),
+                                   _stream_handle(stream, dev))
     _status(lib, "qk_norm_rope_bf16", st)
     return out
 
@@ -428,8 +458,9 @@ def sage_attn_fwd(prepared, S, H, scale, out=None, stream=None):
         _on_stream([out], stream)
     else:
         _check_out("out", out, (B, S, H, D), torch.bfloat16, q_i8.device)
-    st = lib.sage_attn_fwd(*[_ptr(t) for t in prepared], _ptr(out), B, int(S), int(H), D,
-                           float(scale), _stream_handle(stream))
+    with _on_device(q_i8.device):
+        st = lib.sage_attn_fwd(*[_ptr(t) for t in prepared], _ptr(out), B, int(S), int(H), D,
+                               float(scale), _stream_handle(stream, q_i8.device))
     _status(lib, "sage_attn_fwd", st)
     return out
 
@@ -453,9 +484,10 @@ def sage_attn_fwd_ex(prepared, S_q, S_kv, H, H_kv, scale, window=(-1, -1), out=N
         _on_stream([out], stream)
     else:
         _check_out("out", out, (B, S_q, H, D), torch.bfloat16, q_i8.device)
-    st = lib.sage_attn_fwd_ex(*[_ptr(t) for t in prepared], _ptr(out), B, int(S_q), int(S_kv), int(H),
-                              int(H_kv), D, float(scale), int(window[0]), int(window[1]),
-                              _stream_handle(stream))
+    with _on_device(q_i8.device):
+        st = lib.sage_attn_fwd_ex(*[_ptr(t) for t in prepared], _ptr(out), B, int(S_q), int(S_kv), int(H),
+                                  int(H_kv), D, float(scale), int(window[0]), int(window[1]),
+                                  _stream_handle(stream, q_i8.device))
     _status(lib, "sage_attn_fwd_ex", st)
     return out
 

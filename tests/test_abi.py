@@ -208,8 +208,8 @@ def test_binding_rejects_wrong_outputs_before_any_call(monkeypatch):
     monkeypatch.setattr(mod, "load", lambda path=None: FakeLib())
     dev = torch.device("meta")
     q = torch.empty((1, 300, 2, 128), dtype=torch.bfloat16, device=dev)
-    monkeypatch.setattr(mod, "_check_bshd", lambda name, t, dtype: None)
-    monkeypatch.setattr(mod, "_stream_handle", lambda s: None)
+    monkeypatch.setattr(mod, "_check_bshd", lambda name, t, dtype, device=None: None)
+    monkeypatch.setattr(mod, "_stream_handle", lambda s, device=None: None)
     short = torch.empty((1, 299, 2, 128), dtype=torch.bfloat16, device=dev)
     with pytest.raises(ValueError, match="shape"):
         mod.attn_fwd_bf16(q, q, q, 0.088, out=short)
@@ -227,6 +227,53 @@ def test_binding_rejects_wrong_outputs_before_any_call(monkeypatch):
     with pytest.raises(ValueError):
         mod.sage_prepare(q, q, q, 0.088, out=tuple(good[:5]))
     assert calls == []  # nothing reached the library
+
+
+def test_binding_rejects_workspaces_off_the_tensors_device(monkeypatch):
+    """A workspace in host memory (or on another GPU) would hand the kernels a pointer they
+    cannot use: the binding refuses it before any library call."""
+    import torch
+    mod = ia
+    calls = []
+
+    class FakeLib:
+        def __getattr__(self, name):
+            def f(*a):
+                calls.append(name)
+                return 0
+            return f
+
+        def ditattn_sage_padded_len(self, S):  # a size query, not a launch
+            return (S + 255) // 256 * 256
+
+    monkeypatch.setattr(mod, "load", lambda path=None: FakeLib())
+    monkeypatch.setattr(mod, "_check_bshd", lambda name, t, dtype, device=None: None)
+    monkeypatch.setattr(mod, "_stream_handle", lambda s, device=None: None)
+    monkeypatch.setattr(mod, "bf16_workspace_size", lambda *a, **k: 4096)
+    monkeypatch.setattr(mod, "sage_workspace_size", lambda *a, **k: 4096)
+    dev = torch.device("meta")
+    q = torch.empty((1, 300, 2, 128), dtype=torch.bfloat16, device=dev)
+    host_ws = torch.zeros(8192, dtype=torch.uint8)  # host memory
+    with pytest.raises(ValueError, match="workspace"):
+        mod.attn_fwd_bf16_ws(q, q, q, 0.088, workspace=host_ws)
+    with pytest.raises(ValueError, match="workspace"):
+        mod.attn_fwd_bf16_ws(q, q, q, 0.088, workspace=torch.empty(100, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError, match="workspace"):
+        mod.sage_prepare_ex(q, q, q, 0.088, smooth_k=True, workspace=host_ws)
+    assert calls == []
+
+
+def test_check_helpers_reject_other_devices():
+    import torch
+    cpu = torch.zeros((2, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        ia._check_workspace(cpu, 8, torch.device("cuda", 0))
+    with pytest.raises(ValueError):
+        ia._check_workspace(torch.zeros(4, dtype=torch.uint8), 8, torch.device("cpu"))  # too small
+    assert ia._check_workspace(torch.zeros(16, dtype=torch.int32), 64, torch.device("cpu")) == 64
+
+    with pytest.raises(TypeError):  # host tensors are never accepted as inputs
+        ia._check_bshd("k", torch.zeros((1, 1, 1, 128), dtype=torch.bfloat16), torch.bfloat16)
 
 
 # ---------------------------------------------------------------- sage_prepare_ex / qk_norm_rope_bf16
