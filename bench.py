@@ -10,8 +10,9 @@ quarter marks give the first- and last-quarter ms per step (the clock regime).
 The same JSON line carries one row per (workload, mode) for the DiT shapes:
   bf16       attn_fwd_bf16_ws (the plain attn_fwd_bf16 kernel unless the last round of
              query tiles is split)                vs the BF16 MFMA peak
-  sage       sage_prepare + sage_attn_fwd       vs the 8-bit MFMA peak
-  sage_core  sage_attn_fwd on prepared tensors  vs the 8-bit MFMA peak
+  sage       sage_prepare + sage_attn_fwd_ws    vs the 8-bit MFMA peak
+  sage_core  sage_attn_fwd_ws on prepared tensors (the plain sage_attn_fwd kernel
+             unless the last round of query tiles is split)   vs the 8-bit MFMA peak
   prepare    sage_prepare                       vs the HBM peak (algorithmic bytes)
 Rows are timed first, each for at least --row-ms milliseconds, and the headline
 follows the last one with no idle gap (its inputs are made beforehand): the
@@ -212,9 +213,11 @@ class Inputs:
         self.out = torch.empty_like(self.q)
         self._prep = None
         import image_dit_amd as ia
-        # the BF16 rows run attn_fwd_bf16_ws: the last, partial round of query tiles is split over
-        # every CU where that pays (workspace size > 0), else it is the plain attn_fwd_bf16 kernel
-        self.ws_bytes = ia.bf16_workspace_size(w.B, w.S, w.S, w.H, w.H)
+        # the BF16 and Sage rows run the _ws entry points: the last, partial round of query tiles
+        # is split over every CU where that pays (workspace size > 0), else they are the plain
+        # kernels; one workspace serves both (one call at a time)
+        self.ws_bytes = max(ia.bf16_workspace_size(w.B, w.S, w.S, w.H, w.H),
+                            ia.sage_attn_workspace_size(w.B, w.S, w.S, w.H, w.H))
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev) if self.ws_bytes else None
 
     def prepared(self, stream):
@@ -234,11 +237,13 @@ def mode_fn(inp, mode, stream):
     if mode == "prepare":
         return lambda: ia.sage_prepare(inp.q, inp.k, inp.v, w.scale, out=prep, stream=stream)
     if mode == "sage_core":
-        return lambda: ia.sage_attn_fwd(prep, w.S, w.H, w.scale, out=inp.out, stream=stream)
+        return lambda: ia.sage_attn_fwd_ws(prep, w.S, w.S, w.H, w.H, w.scale, out=inp.out, workspace=inp.ws,
+                                           stream=stream)
     if mode == "sage":
         def f():
             ia.sage_prepare(inp.q, inp.k, inp.v, w.scale, out=prep, stream=stream)
-            ia.sage_attn_fwd(prep, w.S, w.H, w.scale, out=inp.out, stream=stream)
+            ia.sage_attn_fwd_ws(prep, w.S, w.S, w.H, w.H, w.scale, out=inp.out, workspace=inp.ws,
+                                stream=stream)
         return f
     raise ValueError(mode)
 

@@ -21,6 +21,7 @@ __all__ = ["DitAttnError", "load", "abi_version", "sage_padded_len", "sage_works
            "attn_fwd_bf16", "attn_fwd_bf16_ex", "sage_prepare", "sage_prepare_ex",
            "qk_norm_rope_bf16", "sage_attn_fwd", "sage_attn_fwd_ex", "sage_attention",
            "sage_attention_ex", "sage_prepare_ex_noalloc", "attn_fwd_bf16_ws", "bf16_workspace_size",
+           "sage_attn_fwd_ws", "sage_attn_workspace_size",
            "STATIC_SCRATCH_BYTES", "HEAD_DIM", "LIB_PATH"]
 
 HEAD_DIM = 128
@@ -63,11 +64,14 @@ def load(path=None):
     lib.ditattn_bf16_workspace_size.argtypes = [ci] * 7
     lib.ditattn_bf16_workspace_size.restype = ctypes.c_size_t
     lib.sage_attn_fwd_ex.argtypes = [vp] * 7 + [ci] * 6 + [cf, ci, ci, vp]
+    lib.sage_attn_fwd_ws.argtypes = [vp] * 7 + [ci] * 6 + [cf, ci, ci, vp, ctypes.c_size_t, vp]
+    lib.ditattn_sage_attn_workspace_size.argtypes = [ci] * 7
+    lib.ditattn_sage_attn_workspace_size.restype = ctypes.c_size_t
     lib.ditattn_sage_workspace_size.argtypes = [ci, ci, ci]
     lib.ditattn_sage_workspace_size.restype = ctypes.c_size_t
     for name in ("attn_fwd_bf16", "sage_prepare", "sage_attn_fwd", "sage_prepare_ex",
                  "qk_norm_rope_bf16", "attn_fwd_bf16_ex", "sage_attn_fwd_ex",
-                 "sage_prepare_ex_noalloc", "attn_fwd_bf16_ws"):
+                 "sage_prepare_ex_noalloc", "attn_fwd_bf16_ws", "sage_attn_fwd_ws"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -489,6 +493,51 @@ def sage_attn_fwd_ex(prepared, S_q, S_kv, H, H_kv, scale, window=(-1, -1), out=N
                                   int(H_kv), D, float(scale), int(window[0]), int(window[1]),
                                   _stream_handle(stream, q_i8.device))
     _status(lib, "sage_attn_fwd_ex", st)
+    return out
+
+
+def sage_attn_workspace_size(B, S_q, S_kv, H, H_kv, window=(-1, -1)):
+    """Bytes of workspace sage_attn_fwd_ws needs on the current device (0: no split)."""
+    return int(load().ditattn_sage_attn_workspace_size(int(B), int(S_q), int(S_kv), int(H), int(H_kv),
+                                                        int(window[0]), int(window[1])))
+
+
+def sage_attn_fwd_ws(prepared, S_q, S_kv, H, H_kv, scale, window=(-1, -1), out=None, workspace=None,
+                     stream=None):
+    """sage_attn_fwd_ex with a workspace that splits the last, partial round of query tiles
+    over every compute unit (see sage_attn_workspace_size).  workspace: a contiguous buffer
+    on the tensors' GPU of at least that many bytes, allocated (zero-filled) here when None.
+    One workspace serves one call at a time."""
+    import torch
+    lib = load()
+    if len(prepared) < 6:
+        raise ValueError("expected the tensors returned by sage_prepare_ex")
+    prepared = tuple(prepared[:6])
+    q_i8 = prepared[0]
+    if not isinstance(q_i8, torch.Tensor) or q_i8.dim() != 4 or q_i8.device.type != "cuda":
+        raise ValueError("prepared tensors must be the GPU tensors returned by sage_prepare_ex")
+    dev = q_i8.device
+    B, D = int(q_i8.shape[0]), int(q_i8.shape[3])
+    for t, (name, shape, dt) in zip(prepared, _prepared_specs(B, int(S_q), int(H), D, int(S_kv), int(H_kv))):
+        _check_out(name, t, shape, dt, dev)
+    if out is None:
+        out = torch.empty((B, S_q, H, D), dtype=torch.bfloat16, device=dev)
+        _on_stream([out], stream)
+    else:
+        _check_out("out", out, (B, S_q, H, D), torch.bfloat16, dev)
+    with _on_device(dev):  # the split plan depends on the device's compute units
+        need = sage_attn_workspace_size(B, S_q, S_kv, H, H_kv, window)
+    ws_bytes = 0
+    if need:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+            _on_stream([workspace], stream)
+        ws_bytes = _check_workspace(workspace, need, dev)
+    with _on_device(dev):
+        st = lib.sage_attn_fwd_ws(*[_ptr(t) for t in prepared], _ptr(out), B, int(S_q), int(S_kv), int(H),
+                                  int(H_kv), D, float(scale), int(window[0]), int(window[1]),
+                                  _ptr(workspace) if need else None, ws_bytes, _stream_handle(stream, dev))
+    _status(lib, "sage_attn_fwd_ws", st)
     return out
 
 

@@ -159,7 +159,7 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o, int B
 size_t ditattn_bf16_workspace_size(int B, int S_q, int S_kv, int H, int H_kv, int window_left,
                                    int window_right) {
   if (check_sizes(B, S_q, S_kv, H, H_kv, 128, 1.0f) != DITATTN_OK) return 0;
-  return ditattn::bf16_split_plan(B, S_q, S_kv, H, window_left, window_right).bytes;
+  return ditattn::split_tail_plan(B, S_q, S_kv, H, window_left, window_right).bytes;
 }
 
 int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int B, int S_q,
@@ -178,7 +178,7 @@ int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int B
     return DITATTN_EINVAL;
   ditattn::Bf16Args a{q, k, v, o, B, S_q, S_kv, H, H_kv, log2e_scale(scale), window_left,
                       window_right, 0, 0, 0};
-  const ditattn::Bf16Split plan = ditattn::bf16_split_plan(B, S_q, S_kv, H, window_left, window_right);
+  const ditattn::SplitPlan plan = ditattn::split_tail_plan(B, S_q, S_kv, H, window_left, window_right);
   if (plan.grid > 0) {
     if (!workspace || workspace_bytes < plan.bytes) return DITATTN_EINVAL;
     if (misaligned(workspace)) return DITATTN_EALIGN;
@@ -301,10 +301,14 @@ int qk_norm_rope_bf16(const void* x, void* out, int B, int S, int H, int D, cons
   return DITATTN_OK;
 }
 
-int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                     const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
-                     int B, int S_q, int S_kv, int H, int H_kv, int D, float scale,
-                     int window_left, int window_right, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks shared by the Sage attention entry points; fills `a` when they pass.
+int sage_attn_args(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                   const uint8_t* v_fp8, const float* v_scale, void* o, int B, int S_q, int S_kv, int H,
+                   int H_kv, int D, float scale, int window_left, int window_right, ditattn::SageArgs& a,
+                   int64_t& o_bytes) {
   int st = check_sizes(B, S_q, S_kv, H, H_kv, D, scale);
   if (st != DITATTN_OK) return st;
   if (window_left < -1 || window_right < -1) return DITATTN_EINVAL;
@@ -320,11 +324,67 @@ int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
   const void* ins[6] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale};
   const int64_t in_bytes[6] = {bhq * sqp * 128, bhq * (sqp / 32) * 4, bhk * skp * 128,
                                bhk * (skp / 32) * 4, bhk * skp * 128, bhk * 128 * 4};
+  o_bytes = bhq * S_q * 256;
   for (int i = 0; i < 6; ++i)
-    if (overlaps(o, bhq * S_q * 256, ins[i], in_bytes[i])) return DITATTN_EINVAL;
-  ditattn::SageArgs a{q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S_q, S_kv, H, H_kv,
-                      static_cast<int>(sqp), static_cast<int>(skp), window_left, window_right,
-                      0, 0, 0};
+    if (overlaps(o, o_bytes, ins[i], in_bytes[i])) return DITATTN_EINVAL;
+  a = ditattn::SageArgs{q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S_q, S_kv, H, H_kv,
+                        static_cast<int>(sqp), static_cast<int>(skp), window_left, window_right,
+                        0, 0, 0};
+  return DITATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                     const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
+                     int B, int S_q, int S_kv, int H, int H_kv, int D, float scale,
+                     int window_left, int window_right, hipStream_t stream) {
+  ditattn::SageArgs a{};
+  int64_t o_bytes = 0;
+  const int st = sage_attn_args(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S_q, S_kv, H, H_kv, D,
+                                scale, window_left, window_right, a, o_bytes);
+  if (st != DITATTN_OK) return st;
+  if (ditattn::launch_sage_attn_fwd(a, stream) != hipSuccess) return DITATTN_EHIP;
+  return DITATTN_OK;
+}
+
+size_t ditattn_sage_attn_workspace_size(int B, int S_q, int S_kv, int H, int H_kv, int window_left,
+                                        int window_right) {
+  if (check_sizes(B, S_q, S_kv, H, H_kv, 128, 1.0f) != DITATTN_OK) return 0;
+  return ditattn::split_tail_plan(B, S_q, S_kv, H, window_left, window_right).bytes;
+}
+
+int sage_attn_fwd_ws(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                     const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
+                     int B, int S_q, int S_kv, int H, int H_kv, int D, float scale,
+                     int window_left, int window_right, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  ditattn::SageArgs a{};
+  int64_t o_bytes = 0;
+  const int st = sage_attn_args(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o, B, S_q, S_kv, H, H_kv, D,
+                                scale, window_left, window_right, a, o_bytes);
+  if (st != DITATTN_OK) return st;
+  const ditattn::SplitPlan plan = ditattn::split_tail_plan(B, S_q, S_kv, H, window_left, window_right);
+  if (plan.grid > 0) {
+    if (!workspace || workspace_bytes < plan.bytes) return DITATTN_EINVAL;
+    if (misaligned(workspace)) return DITATTN_EALIGN;
+    const int64_t wb = static_cast<int64_t>(plan.bytes);
+    const int64_t sqp = padded(S_q), skp = padded(S_kv);
+    const int64_t bhq = static_cast<int64_t>(B) * H, bhk = static_cast<int64_t>(B) * H_kv;
+    const void* all[7] = {q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o};
+    const int64_t all_bytes[7] = {bhq * sqp * 128, bhq * (sqp / 32) * 4, bhk * skp * 128,
+                                  bhk * (skp / 32) * 4, bhk * skp * 128, bhk * 128 * 4, o_bytes};
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(workspace, wb, all[i], all_bytes[i])) return DITATTN_EINVAL;
+    a.sk_grid = plan.grid;
+    a.sk_rounds = plan.rounds;
+    a.sk_nk = plan.nk;
+    a.sk_tail_units = plan.tail_units;
+    a.ws_flag = static_cast<uint32_t*>(workspace);
+    a.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.flag_bytes);
+    a.epoch = next_epoch();
+  }
   if (ditattn::launch_sage_attn_fwd(a, stream) != hipSuccess) return DITATTN_EHIP;
   return DITATTN_OK;
 }

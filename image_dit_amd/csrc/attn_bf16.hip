@@ -86,29 +86,17 @@ __device__ __forceinline__ int key_hi(const Bf16Args& a, int i) {
   return (int)(hi < -1 ? -1 : (hi > a.S_kv - 1 ? a.S_kv - 1 : hi));
 }
 
-// How a run over a key-tile range ends (split tails, see attn_body<true>).
-enum { kFull = 0, kPartial = 1, kOwner = 2 };
-constexpr int kPartRegs = 66;  // per thread: 64 accumulator values, m, l
-
-// Spin on a partial's ready flag (written by a lower-numbered workgroup, which never waits on
-// this one); gives up after about a second so that every wave exits whatever happens.
-__device__ __forceinline__ bool wait_flag(const uint32_t* flag, uint32_t epoch) {
-  for (int it = 0; it < (1 << 21); ++it) {
-    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == epoch) return true;
-    __builtin_amdgcn_s_sleep(8);
-  }
-  return false;
-}
+static_assert(NW * 64 == kSplitThreads, "split-tail slots hold one row per thread");
 
 template <bool SK>
 __device__ __forceinline__ void attn_body(const Bf16Args& a) {
   constexpr int BQ = NW * 32;
   __shared__ __attribute__((aligned(16))) char lds[4 * TILE_BYTES];  // K stage 0, 1, V stage 0, 1
-  __shared__ int ready_all;
 
   // One query tile L: the key tiles its window covers (tb < 0), or the tiles [tb, te) of a split
-  // tail, ending by mode: kFull writes O, kPartial writes (acc, m, l) to the workgroup's slot and
-  // raises its flag, kOwner first merges the slots of workgroups p_lo .. p_hi, then writes O.
+  // tail, ending by mode: kSplitFull writes O, kSplitPartial writes (acc, m, l) to the
+  // workgroup's slot and raises its flag, kSplitOwner first merges the slots of workgroups
+  // p_lo .. p_hi, then writes O.
   auto run = [&](int L, int tb, int te, int mode, int p_lo, int p_hi) {
   const int bh = L / a.num_qt;
   int qt = L - bh * a.num_qt;
@@ -436,57 +424,12 @@ __device__ __forceinline__ void attn_body(const Bf16Args& a) {
 
   // ---- epilogue
   mfma_drain(acc[0], acc[1], acc[2], acc[3]);
-  const int tid_ = threadIdx.x;
-  // a workgroup's slot: kPartRegs rows of NW * 64 floats (register-major: every access is
-  // coalesced; buffer accesses keep the per-row offset in a scalar)
-  auto slot_rsrc = [&](int gi) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.ws_part + (int64_t)gi * kPartRegs * (NW * 64)), (short)0,
-                                             kPartRegs * (NW * 64) * 4, 0x00020000);
-  };
-  constexpr int kRowBytes = NW * 64 * 4;
-  // Partials and flags move with system-coherent accesses (sc0 sc1: through to the point of
-  // coherence of all XCDs, past both cache levels), ordered by vmcnt waits; no cache-wide
-  // write-back or invalidation, which would evict the K/V tiles the other workgroups stream.
-  constexpr int kCoherent = 1 | 16;  // cache policy bits sc0, sc1
-  if (mode == kPartial) {  // (acc, m, l) of this lane
-    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(blockIdx.x);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[dt][r]), rs, tid_ * 4, (16 * dt + r) * kRowBytes,
-                                              kCoherent);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs, tid_ * 4, 64 * kRowBytes, kCoherent);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lsum), rs, tid_ * 4, 65 * kRowBytes, kCoherent);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have completed
-    __syncthreads();
-    if (tid_ == 0) __hip_atomic_store(a.ws_flag + blockIdx.x, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (mode == kSplitPartial) {
+    split_write_partial(a.ws_part, a.ws_flag, a.epoch, acc, m, lsum);
     return;
   }
   bool ok = true;
-  if (mode == kOwner) {  // merge the other pieces of this query tile, lowest workgroup first
-    for (int g = p_lo; g <= p_hi; ++g) {
-      if (tid_ == 0) ready_all = wait_flag(a.ws_flag + g, a.epoch) ? 1 : 0;
-      __syncthreads();
-      ok = ok && ready_all != 0;
-      const __amdgpu_buffer_rsrc_t rs = slot_rsrc(g);
-      const float mp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, tid_ * 4, 64 * kRowBytes, kCoherent));
-      const float lp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, tid_ * 4, 65 * kRowBytes, kCoherent));
-      const float mn = fmaxf(m, mp);
-      const float sa = m == -INFINITY ? 0.0f : fast_exp2(m - mn);
-      const float sb = mp == -INFINITY ? 0.0f : fast_exp2(mp - mn);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[dt][r] = acc[dt][r] * sa +
-                       __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, tid_ * 4, (16 * dt + r) * kRowBytes,
-                                                                            kCoherent)) * sb;
-      lsum = lsum * sa + lp * sb;
-      m = mn;
-      __syncthreads();  // ready_all is rewritten for the next piece
-    }
-  }
+  if (mode == kSplitOwner) ok = split_merge(a.ws_part, a.ws_flag, a.epoch, p_lo, p_hi, acc, m, lsum);
   // O = acc / l, BF16, rows < S_q (0 for a row with no visible key; NaN if a piece never came)
   const float lt = half_pair_sum(lsum);
   const float inv = !ok ? __builtin_nanf("") : (lt > 0.0f ? 1.0f / lt : 0.0f);
@@ -504,45 +447,8 @@ __device__ __forceinline__ void attn_body(const Bf16Args& a) {
   }
   };  // run
 
-  if constexpr (!SK) {
-    run(xcd_remap(blockIdx.x, a.n_tiles), -1, -1, kFull, 0, -1);
-  } else {
-    // Split tail (key windows off, every query tile has nk key tiles): the grid is one workgroup
-    // per CU.  Rounds 0 .. R-1 give each workgroup whole query tiles; the rest, U_tail tiles of nk
-    // key tiles each, is cut into equal ranges of (query tile, key tile) units, range g to
-    // workgroup g.  A range's pieces run last first: the last one, when it stops inside a query
-    // tile, is that tile's partial (written to slot g); a piece that ends at its tile's last key
-    // tile owns the tile and merges the partials of the lower workgroups that cover the rest.
-    const int G = gridDim.x, g = blockIdx.x, nk = a.sk_nk;
-    const int64_t T = a.sk_tail_units;
-    const int64_t s0 = T * g / G, e0 = T * (g + 1) / G;
-    const int base = a.sk_rounds * G;
-    // work items: rounds 0 .. R-1, then the tail pieces from the last query tile down
-    const int64_t u_hi = e0 > s0 ? (e0 - 1) / nk : 0, u_lo = s0 / nk;
-    const int n_items = a.sk_rounds + (e0 > s0 ? (int)(u_hi - u_lo + 1) : 0);
-    for (int it = 0; it < n_items; ++it) {
-      int L, tb = 0, te = nk, mode = kFull, p_lo = 0, p_hi = -1;
-      if (it < a.sk_rounds) {
-        L = it * G + xcd_remap(g, G);
-      } else {
-        const int64_t u = u_hi - (it - a.sk_rounds);
-        const int64_t ub = u * nk;
-        tb = (int)((s0 > ub ? s0 : ub) - ub);
-        te = (int)((e0 < ub + nk ? e0 : ub + nk) - ub);
-        L = base + (int)u;
-        if (te < nk) {
-          mode = kPartial;
-        } else if (tb > 0) {
-          mode = kOwner;
-          p_hi = g - 1;
-          p_lo = g - 1;
-          while (p_lo > 0 && T * p_lo / G > ub) --p_lo;  // the workgroup whose range holds ub
-        }
-      }
-      run(L, tb, te, mode, p_lo, p_hi);
-      __syncthreads();
-    }
-  }
+  if constexpr (!SK) run(xcd_remap(blockIdx.x, a.n_tiles), -1, -1, kSplitFull, 0, -1);
+  else split_tail_items(a.sk_rounds, a.sk_nk, a.sk_tail_units, run);
 }
 
 __global__ void __launch_bounds__(NW * 64, DITATTN_BF16_OCC) attn_fwd_bf16_kernel(Bf16Args a) {
@@ -572,12 +478,13 @@ int cu_count() {
 }
 }  // namespace
 
-// Split-tail plan: used when the key windows are off, there are at least three whole rounds
-// of query tiles and the last round would leave more than 5 % of the CU-rounds idle.  With
+// Split-tail plan of either attention kernel (both tile queries by 256 rows and keys by 64):
+// used when the key windows are off, there are at least three whole rounds of query tiles and
+// the last round would leave more than 5 % of the CU-rounds idle.  With
 // fewer whole rounds the tail's pieces, start-ups and merges cost more than the idle CUs of a
 // plain last round (measured: the board's clock rises while they idle).
-Bf16Split bf16_split_plan(int B, int S_q, int S_kv, int H, int wl, int wr) {
-  Bf16Split p{};
+SplitPlan split_tail_plan(int B, int S_q, int S_kv, int H, int wl, int wr) {
+  SplitPlan p{};
   const int G = cu_count();
   const int64_t U = (int64_t)B * H * ((S_q + kBf16BQ - 1) / kBf16BQ);
   const int nk = (S_kv + bf16attn::BK - 1) / bf16attn::BK;
@@ -589,7 +496,7 @@ Bf16Split bf16_split_plan(int B, int S_q, int S_kv, int H, int wl, int wr) {
   p.nk = nk;
   p.tail_units = (U - (int64_t)p.rounds * G) * nk;
   p.flag_bytes = ((size_t)G * 4 + 255) / 256 * 256;
-  p.bytes = p.flag_bytes + (size_t)G * bf16attn::kPartRegs * bf16attn::NW * 64 * sizeof(float);
+  p.bytes = p.flag_bytes + (size_t)G * kSplitSlotRows * kSplitThreads * sizeof(float);
   return p;
 }
 

@@ -111,11 +111,18 @@ __device__ __forceinline__ int key_hi(const SageArgs& a, int i) {
   return (int)(hi < -1 ? -1 : (hi > a.S_kv - 1 ? a.S_kv - 1 : hi));
 }
 
-__global__ void __launch_bounds__(NW * 64, 1)
-sage_attn_fwd_kernel(SageArgs a) {
+static_assert(NW * 64 == kSplitThreads && BQ == 256 && BK == 64,
+              "the split-tail plan and slots assume the BF16 kernel's tiling");
+
+template <bool SK>
+__device__ __forceinline__ void sage_body(const SageArgs& a) {
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * (KT_BYTES + VT_BYTES) + NSTAGE * 16];  // 48 KB
 
-  int L = xcd_remap(blockIdx.x, a.n_tiles);
+  // One query tile L: the key tiles its window covers (tb < 0), or the tiles [tb, te) of a split
+  // tail, ending by mode: kSplitFull writes O, kSplitPartial writes (acc, m, l) to the
+  // workgroup's slot and raises its flag, kSplitOwner first merges the slots of workgroups
+  // p_lo .. p_hi, then writes O.
+  auto run = [&](int L, int tb, int te, int mode, int p_lo, int p_hi) __attribute__((always_inline)) {
   const int bh = L / a.num_qt;
   int qt = L - bh * a.num_qt;
   if (a.reverse) qt = a.num_qt - 1 - qt;  // longest key ranges first (causal)
@@ -147,8 +154,8 @@ sage_attn_fwd_kernel(SageArgs a) {
   const int lo_i = key_lo(a, qi), hi_i = key_hi(a, qi);
   const int lo_first = key_lo(a, i_first), lo_last = key_lo(a, i_last);
   const int hi_first = key_hi(a, i_first), hi_last = key_hi(a, i_last);
-  const int t0 = lo_first / BK;
-  const int t1 = hi_last >= 0 ? hi_last / BK + 1 : 0;
+  const int t0 = tb >= 0 ? tb : lo_first / BK;
+  const int t1 = tb >= 0 ? te : (hi_last >= 0 ? hi_last / BK + 1 : 0);
   const int n = t1 - t0;  // tiles this workgroup visits (uniform)
   // a tile needs no mask when every key of it is visible to every row of the workgroup
   auto masked_tile = [&](int t) __attribute__((always_inline)) { return t * BK < lo_last || t * BK + BK - 1 > hi_first; };
@@ -473,8 +480,15 @@ sage_attn_fwd_kernel(SageArgs a) {
   // ---- epilogue: O[i][d] = acc * v_scale[d] / l (0 for a row with no visible key)
   mfma_drain(acc[0], acc[1], acc[2], acc[3]);
   mfma_drain(lacc);
-  const float lsum = lacc[0];
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  float lsum = lacc[0];
+  if (mode == kSplitPartial) {
+    split_write_partial(a.ws_part, a.ws_flag, a.epoch, acc, m, lsum);
+    return;
+  }
+  bool ok = true;
+  if (mode == kSplitOwner) ok = split_merge(a.ws_part, a.ws_flag, a.epoch, p_lo, p_hi, acc, m, lsum);
+  // (NaN if a piece never came)
+  const float inv = !ok ? __builtin_nanf("") : (lsum > 0.0f ? 1.0f / lsum : 0.0f);
   if (qi < a.S_q) {
     const float* vsc = a.v_scale + (int64_t)bhk * kHeadDim;
     __bf16* orow = (__bf16*)a.o + (((int64_t)b * a.S_q + qi) * a.H + h) * kHeadDim;
@@ -490,7 +504,14 @@ sage_attn_fwd_kernel(SageArgs a) {
         *(bf16x4*)(orow + d) = ov;
       }
   }
+  };  // run
+
+  if constexpr (!SK) run(xcd_remap(blockIdx.x, a.n_tiles), -1, -1, kSplitFull, 0, -1);
+  else split_tail_items(a.sk_rounds, a.sk_nk, a.sk_tail_units, run);
 }
+
+__global__ void __launch_bounds__(NW * 64, 1) sage_attn_fwd_kernel(SageArgs a) { sage_body<false>(a); }
+__global__ void __launch_bounds__(NW * 64, 1) sage_attn_fwd_split_kernel(SageArgs a) { sage_body<true>(a); }
 
 }  // namespace sageattn
 
@@ -499,6 +520,8 @@ hipError_t launch_sage_attn_fwd(const SageArgs& a0, hipStream_t stream) {
   a.num_qt = (a.S_q + sageattn::BQ - 1) / sageattn::BQ;
   a.n_tiles = a.B * a.H * a.num_qt;
   a.reverse = a.wr >= 0 ? 1 : 0;  // a key range that ends at the query: later tiles see more keys
+  if (a.sk_grid > 0)
+    return launch(sageattn::sage_attn_fwd_split_kernel, dim3(a.sk_grid), dim3(sageattn::NW * 64), stream, a);
   return launch(sageattn::sage_attn_fwd_kernel, dim3(a.n_tiles), dim3(sageattn::NW * 64), stream, a);
 }
 

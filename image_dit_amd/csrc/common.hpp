@@ -166,6 +166,89 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c, 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale, 0, scale);
 }
 
+// ---------------------------------------------------------------- split tail
+// Both attention kernels can run a grid of one workgroup per compute unit: rounds of whole
+// query tiles first, then the remaining (query tile, key tile) units cut into equal ranges,
+// one per workgroup.  A piece that stops inside its query tile leaves FP32 partials in the
+// workgroup's slot of a caller-owned workspace -- per thread of the 8-wave workgroup: its 64
+// accumulator values, the running max m and the row sum l -- and raises the slot's flag to
+// the call's epoch; the piece that ends at the tile's last key tile merges the partials of the
+// lower-numbered workgroups that cover the rest of the tile, lowest first, and writes O.
+enum { kSplitFull = 0, kSplitPartial = 1, kSplitOwner = 2 };
+constexpr int kSplitSlotRows = 66;      // per thread: 64 accumulator values, m, l
+constexpr int kSplitThreads = 512;      // threads of an attention workgroup (8 waves)
+constexpr int kSplitRowBytes = kSplitThreads * 4;
+// Partials and flags move with system-coherent accesses (sc0 sc1: through to the point of
+// coherence of all XCDs, past both cache levels), ordered by vmcnt waits; no cache-wide
+// write-back or invalidation, which would evict the K/V tiles the other workgroups stream.
+constexpr int kSplitCoherent = 1 | 16;  // cache policy bits sc0, sc1
+
+// Spin on a partial's ready flag (written by a lower-numbered workgroup, which never waits on
+// this one); gives up after about a second so that every wave exits whatever happens.
+__device__ __forceinline__ bool split_wait_flag(const uint32_t* flag, uint32_t epoch) {
+  for (int it = 0; it < (1 << 21); ++it) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == epoch) return true;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  return false;
+}
+
+// Workgroup g's slot: kSplitSlotRows rows of kSplitThreads floats (register-major, so every
+// access is coalesced and a buffer access keeps the row offset in a scalar).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t split_slot(const float* part, int g) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(part + (int64_t)g * kSplitSlotRows * kSplitThreads), (short)0,
+                                           kSplitSlotRows * kSplitRowBytes, 0x00020000);
+}
+
+// This workgroup's partial (acc, m, l of every thread) to its slot, then its flag.
+__device__ __forceinline__ void split_write_partial(float* part, uint32_t* flags, uint32_t epoch,
+                                                    const f32x16 (&acc)[4], float m, float l) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = split_slot(part, blockIdx.x);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[dt][r]), rs, tid * 4, (16 * dt + r) * kSplitRowBytes,
+                                            kSplitCoherent);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs, tid * 4, 64 * kSplitRowBytes, kSplitCoherent);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rs, tid * 4, 65 * kSplitRowBytes, kSplitCoherent);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have completed
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(flags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Merge the partials of workgroups p_lo .. p_hi (lowest first) into this thread's (acc, m, l),
+// the blocked form's rescale by 2^(m_old - m_new); false when a piece never came.
+__device__ __forceinline__ bool split_merge(const float* part, const uint32_t* flags, uint32_t epoch, int p_lo,
+                                            int p_hi, f32x16 (&acc)[4], float& m, float& l) {
+  __shared__ int ready_all;
+  const int tid = threadIdx.x;
+  bool ok = true;
+  for (int g = p_lo; g <= p_hi; ++g) {
+    if (tid == 0) ready_all = split_wait_flag(flags + g, epoch) ? 1 : 0;
+    __syncthreads();
+    ok = ok && ready_all != 0;
+    const __amdgpu_buffer_rsrc_t rs = split_slot(part, g);
+    const float mp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, 64 * kSplitRowBytes, kSplitCoherent));
+    const float lp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, 65 * kSplitRowBytes, kSplitCoherent));
+    const float mn = fmaxf(m, mp);
+    const float sa = m == -INFINITY ? 0.0f : fast_exp2(m - mn);
+    const float sb = mp == -INFINITY ? 0.0f : fast_exp2(mp - mn);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc[dt][r] = acc[dt][r] * sa +
+                     __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, (16 * dt + r) * kSplitRowBytes,
+                                                                          kSplitCoherent)) * sb;
+    l = l * sa + lp * sb;
+    m = mn;
+    __syncthreads();  // ready_all is rewritten for the next piece
+  }
+  return ok;
+}
+
 // Workgroup index remapped so that consecutive logical tiles land on the same
 // XCD: the dispatcher deals workgroups round-robin over the 8 XCDs, so
 // physical block w runs on XCD w % 8.  Logical tiles [prefix(x), prefix(x+1))
@@ -174,6 +257,46 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
   const int x = w & 7, slot = w >> 3;
   const int q = n >> 3, rem = n & 7;
   return x * q + (x < rem ? x : rem) + slot;
+}
+
+// The work items of split-tail workgroup blockIdx.x (every query tile has nk key tiles):
+// rounds 0 .. rounds-1 give each workgroup whole query tiles; the rest, tail_units (query
+// tile, key tile) units, is cut into equal ranges, range g to workgroup g.  A range's pieces
+// run last first: the last one, when it stops inside a query tile, is that tile's partial; a
+// piece that ends at its tile's last key tile owns the tile and merges the partials of the
+// lower workgroups that cover the rest.  run(L, tb, te, mode, p_lo, p_hi) processes key tiles
+// [tb, te) of query tile L (tb < 0: its whole key range).
+template <typename Run>
+__device__ __forceinline__ void split_tail_items(int rounds, int nk, int64_t tail_units, Run&& run) {
+  const int G = gridDim.x, g = blockIdx.x;
+  const int64_t T = tail_units;
+  const int64_t s0 = T * g / G, e0 = T * (g + 1) / G;
+  const int base = rounds * G;
+  // work items: rounds 0 .. R-1, then the tail pieces from the last query tile down
+  const int64_t u_hi = e0 > s0 ? (e0 - 1) / nk : 0, u_lo = s0 / nk;
+  const int n_items = rounds + (e0 > s0 ? (int)(u_hi - u_lo + 1) : 0);
+  for (int it = 0; it < n_items; ++it) {
+    int L, tb = 0, te = nk, mode = kSplitFull, p_lo = 0, p_hi = -1;
+    if (it < rounds) {
+      L = it * G + xcd_remap(g, G);
+    } else {
+      const int64_t u = u_hi - (it - rounds);
+      const int64_t ub = u * nk;
+      tb = (int)((s0 > ub ? s0 : ub) - ub);
+      te = (int)((e0 < ub + nk ? e0 : ub + nk) - ub);
+      L = base + (int)u;
+      if (te < nk) {
+        mode = kSplitPartial;
+      } else if (tb > 0) {
+        mode = kSplitOwner;
+        p_hi = g - 1;
+        p_lo = g - 1;
+        while (p_lo > 0 && T * p_lo / G > ub) --p_lo;  // the workgroup whose range holds ub
+      }
+    }
+    run(L, tb, te, mode, p_lo, p_hi);
+    __syncthreads();
+  }
 }
 
 }  // namespace ditattn

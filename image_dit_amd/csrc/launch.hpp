@@ -25,13 +25,14 @@ struct Bf16Args {
   uint32_t epoch;
 };
 
-// Split-tail plan of a BF16 call (grid = 0: not split); bytes = workspace it needs.
-struct Bf16Split {
+// Split-tail plan of an attention call (grid = 0: not split); bytes = workspace it needs.
+// Both attention kernels tile alike (256 query rows, 64 keys, 8 waves), so one plan serves both.
+struct SplitPlan {
   int grid, rounds, nk;
   int64_t tail_units;
   size_t flag_bytes, bytes;
 };
-Bf16Split bf16_split_plan(int B, int S_q, int S_kv, int H, int wl, int wr);
+SplitPlan split_tail_plan(int B, int S_q, int S_kv, int H, int wl, int wr);
 
 hipError_t launch_attn_fwd_bf16(const Bf16Args& a, hipStream_t stream);
 
@@ -75,6 +76,12 @@ struct SageArgs {
   int B, S_q, S_kv, H, H_kv, S_q_pad, S_kv_pad;
   int wl, wr;             // key window (-1 = unbounded on that side)
   int num_qt, n_tiles, reverse;  // filled in by the launcher
+  // split tail (sk_grid > 0): workspace flags and partial slots, per-call epoch
+  int sk_grid, sk_rounds, sk_nk;
+  int64_t sk_tail_units;
+  uint32_t* ws_flag;
+  float* ws_part;
+  uint32_t epoch;
 };
 
 hipError_t launch_sage_attn_fwd(const SageArgs& a, hipStream_t stream);

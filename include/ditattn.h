@@ -274,8 +274,8 @@ int qk_norm_rope_bf16(const void* x, void* out, int B, int S, int H, int D, cons
  *   scale  : checked (finite, > 0) but otherwise unused: sage_prepare already
  *            folded scale * log2(e) into q_scale.
  * Scores s = int32(q_code . k_code) * q_scale * k_scale are in base-2 units.
- * Keys j >= S are masked.  P is rounded to FP8 e4m3 as p * 2^8; the row sum
- * uses the FP32 values; o = acc * v_scale / (l * 2^8).
+ * Keys j >= S are masked.  P is rounded to FP8 e4m3 as p * 2^8 and the row sum
+ * l is taken over the same FP8 values; o = acc * v_scale / l.
  */
 int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                   const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
@@ -293,6 +293,34 @@ int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
                      const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
                      int B, int S_q, int S_kv, int H, int H_kv, int D, float scale,
                      int window_left, int window_right, hipStream_t stream);
+
+/*
+ * sage_attn_fwd_ws -- sage_attn_fwd_ex with a workspace that lets the last, partial round
+ * of query tiles be split over every compute unit, as attn_fwd_bf16_ws does for the BF16
+ * path (same plan: both kernels tile queries by 256 rows and keys by 64).  Same operation,
+ * arguments, checks and status codes as sage_attn_fwd_ex, plus:
+ *   workspace        device pointer, 16-byte aligned, overlapping no tensor, at least
+ *                    ditattn_sage_attn_workspace_size(...) bytes (owned by the caller;
+ *                    zero-filled once before first use is recommended); may be NULL
+ *                    when that size is 0
+ *   workspace_bytes  its size; too small -> DITATTN_EINVAL before anything is enqueued
+ * When the size is 0 (key window on, fewer than three rounds of query tiles, or a last
+ * round that already fills the GPU) the call is sage_attn_fwd_ex.  Otherwise a query tile
+ * split over several workgroups is merged, in a fixed order, from FP32 partials (m, l, acc)
+ * by the workgroup holding its last key tile.  The result meets sage_attn_fwd_ex's accuracy
+ * (it differs from it by P's FP8 rounding, taken relative to each piece's own running max)
+ * and is run-to-run deterministic.  One workspace serves one call at a time.
+ */
+int sage_attn_fwd_ws(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                     const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
+                     int B, int S_q, int S_kv, int H, int H_kv, int D, float scale,
+                     int window_left, int window_right, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Workspace bytes sage_attn_fwd_ws needs on the current device (0: no split; also 0 for
+ * sizes the library rejects).  Equal to ditattn_bf16_workspace_size for the same shape. */
+size_t ditattn_sage_attn_workspace_size(int B, int S_q, int S_kv, int H, int H_kv, int window_left,
+                                        int window_right);
 
 #ifdef __cplusplus
 }

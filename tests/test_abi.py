@@ -366,6 +366,60 @@ def test_noalloc_rejects_before_any_hip_call(lib):
     assert call(H=3, H_kv=2) == EINVAL
 
 
+# ---------------------------------------------------------------- sage_attn_fwd_ws
+def test_sage_ws_rejects_before_any_hip_call(lib):
+    vp = ctypes.c_void_p
+    ptrs = [GOOD * 2 ** (20 + i) for i in range(7)]  # q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, o
+
+    def call(B=1, S=64, H=2, D=128, wl=-1, wr=-1, o=None):
+        p = list(ptrs)
+        if o is not None:
+            p[6] = o
+        return lib.sage_attn_fwd_ws(*[vp(x) for x in p], B, S, S, H, H, D, ctypes.c_float(0.088), wl, wr,
+                                    None, 0, None)
+    assert call(D=64) == EUNSUPPORTED
+    assert call(wl=-2) == EINVAL
+    assert call(o=ptrs[6] + 2) == EALIGN
+    assert call(o=ptrs[0]) == EINVAL  # output over the Q codes
+    assert call(H=MAX_HEADS + 1) == EOVERFLOW
+    # without a GPU the plan is "no split": the size is 0, equal to the BF16 path's
+    for args in ((1, 4608, 4608, 24, 24, -1, -1), (1, 16896, 16896, 24, 24, -1, -1), (1, 0, 64, 2, 2, -1, -1)):
+        assert lib.ditattn_sage_attn_workspace_size(*args) == lib.ditattn_bf16_workspace_size(*args)
+
+
+def test_binding_sage_ws_rejects_host_workspace(monkeypatch):
+    import torch
+    mod = ia
+    calls = []
+
+    class FakeLib:
+        def __getattr__(self, name):
+            def f(*a):
+                calls.append(name)
+                return 0
+            return f
+
+        def ditattn_sage_padded_len(self, S):  # a size query, not a launch
+            return (S + 255) // 256 * 256
+
+    monkeypatch.setattr(mod, "load", lambda path=None: FakeLib())
+    monkeypatch.setattr(mod, "_stream_handle", lambda s, device=None: None)
+    monkeypatch.setattr(mod, "sage_attn_workspace_size", lambda *a, **k: 4096)
+    monkeypatch.setattr(mod, "_on_device", lambda d: __import__("contextlib").nullcontext())
+
+    class Cuda(torch.Tensor):  # meta tensors that report a GPU device
+        @property
+        def device(self):
+            return torch.device("cuda", 0)
+    specs = mod._prepared_specs(1, 300, 2, 128)
+    prepared = tuple(torch.empty(shape, dtype=dt, device="meta").as_subclass(Cuda) for _, shape, dt in specs)
+    out = torch.empty((1, 300, 2, 128), dtype=torch.bfloat16, device="meta").as_subclass(Cuda)
+    with pytest.raises(ValueError, match="workspace"):
+        mod.sage_attn_fwd_ws(prepared, 300, 300, 2, 2, 0.088, out=out,
+                             workspace=torch.zeros(8192, dtype=torch.uint8))
+    assert calls == []
+
+
 # ---------------------------------------------------------------- attn_fwd_bf16_ws
 def test_bf16_ws_rejects_before_any_hip_call(lib):
     vp = ctypes.c_void_p

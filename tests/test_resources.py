@@ -27,6 +27,7 @@ ATTENTION = {  # kernel name fragment -> max LDS bytes per workgroup
     "attn_fwd_bf16_kernel": 65536 + 64,
     "attn_fwd_bf16_split_kernel": 65536 + 64,
     "sage_attn_fwd_kernel": 3 * (8192 + 8192) + 64,
+    "sage_attn_fwd_split_kernel": 3 * (8192 + 8192) + 64,
 }
 
 
@@ -72,11 +73,12 @@ def test_every_kernel_is_reported(reports):
         assert frag in names, frag
 
 
-# The split-tail kernel runs the whole attention body once per work item in a loop, with the
+# The split-tail kernels run the whole attention body once per work item in a loop, with the
 # item's plan (tile, key range, merge range) live beside the body's own scalars: the compiler
-# keeps about 90 scalars in VGPR lanes (v_writelane / v_readlane, no scratch memory).  The
-# allowance caps that at its current size; every other kernel keeps everything in SGPRs.
-SGPR_LANE_SPILL_ALLOWANCE = {"attn_fwd_bf16_split_kernel": 96}
+# keeps some scalars in VGPR lanes (v_writelane / v_readlane, no scratch memory), outside the
+# key loop.  The allowance caps that at its current size; every other kernel keeps everything
+# in SGPRs.
+SGPR_LANE_SPILL_ALLOWANCE = {"attn_fwd_bf16_split_kernel": 96, "sage_attn_fwd_split_kernel": 64}
 
 
 def test_no_spills_no_scratch(reports):
