@@ -22,8 +22,18 @@
 //     s = q_scale * k_scale, already in base-2 units.  The accumulators start
 //     at the bit pattern of 1/(2 pi), so an int32 sum read
 //     as fp32 is exactly 1/(2 pi) + score * 2^-26: the row max is taken on those
-//     bit patterns and p = exp2(score * s - m + 8) is one FMA and one exp2, no
-//     conversion.
+//     bit patterns, and the base-2 argument x = score * s - m + 8 of p * 2^8 is
+//     one FMA on them, no conversion.
+//   * P's e4m3 codes come from x directly, with no exponential: inside one
+//     octave the e4m3 values are evenly spaced, 2^(E-7) (1 + M/8), so the code
+//     8 E + M = 8 (x + 7), rounded, is the e4m3 number with exponent floor(x)
+//     and mantissa frac(x) in eighths: 2^x with its in-octave factor 2^f taken
+//     as 1 + f (at most 6.2 % high).  One FMA makes 8 x + 56 less a centring
+//     offset of 0.35 code steps and one v_cvt_pk_u8_f32 rounds it into its
+//     byte (clamped at 0: p * 2^8 below 2^-7 becomes 0).  Two vector
+//     instructions per score instead of FMA, exp2 and half an FP8 packing;
+//     the relative L2 error of O against exact attention rises from about
+//     0.042 to 0.045 (gate 0.05).
 //   * Matrix phase reads are issued as explicit LDS instructions ahead of the
 //     MFMAs that take them: four K fragments, the tile's k_scale pair and two
 //     V^T fragments at the start of the phase, then one K fragment (later two
@@ -69,6 +79,10 @@ constexpr float kPScaleLog2 = 8.0f;  // P is stored as p * 2^8
 // The running max is raised only when a row's tile max exceeds it by more than
 // this (base-2 units).  P then stays <= 2^0.8, so p * 2^8 <= 445.7 fits e4m3.
 constexpr float kLazyThresh = 0.8f;
+// e4m3 code of p * 2^8 = 2^x: 8 (x + 7) (eight codes per octave, exponent bias 7), less 0.35 of a
+// code step, which centres the error of the in-octave factor 1 + f against 2^f (0 to +0.69 steps).
+constexpr float kCodeSlope = 8.0f;
+constexpr float kCodeOffset = 56.0f - 0.35f;
 // K Q^T accumulator seed: the bit pattern of 1/(2 pi) (0x3E22F983).  Its mantissa field, 2293123,
 // stays inside [0, 2^23) after adding any score (|score| <= 128 * 127^2 = 2064512): the int32
 // sum read as fp32 is exactly kSeed + score * 2^-26.
@@ -167,8 +181,8 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
   lacc = f32x16{};
   float m = -INFINITY;
   // Kept with m (which changes only when the running max is raised): m + kLazyThresh, and the
-  // exp2 offset 8 - m (0 while a row has no visible key, m = -inf).
-  float m_thr = -INFINITY, mneg = 0.0f;
+  // code offset kCodeOffset + 8 (8 - m) (kCodeOffset while a row has no visible key, m = -inf).
+  float m_thr = -INFINITY, mneg = kCodeOffset;
   const int unit_scale = unit_e8m0_scale();
   i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                 0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
@@ -343,7 +357,7 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
     // ---- softmax of the scores of tile t (in si): lazily raised running max, P -> e4m3.
     // One body for every tile (two copies of it make the compiler double-allocate the
     // accumulators); a tile crossing a mask boundary only takes two small branches: its
-    // hidden scores become INT32_MIN before the row max, and their p become 0 after exp2.
+    // hidden scores become INT32_MIN before the row max, and their P codes become 0.
     auto softmax = [&](int t) __attribute__((always_inline)) {
       const float s = s_tile;
       const bool masked = masked_tile(t);  // uniform
@@ -353,37 +367,40 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
         const float alpha = m_new == m ? 1.0f : fast_exp2(m - m_new);
         m = m_new;
         m_thr = m + kLazyThresh;
-        mneg = m == -INFINITY ? 0.0f : kPScaleLog2 - m;  // rows with no visible key yet
+        mneg = m == -INFINITY ? kCodeOffset : fmaf(kCodeSlope, kPScaleLog2 - m, kCodeOffset);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
         lacc *= alpha;
       }
-      // x = score * q_scale * k_scale - m + 8 as ONE fma on the seeded pattern
-      // A = kSeed + score * 2^-26 with s = q_scale * k_scale * 2^26: A * s + (mneg - kSeed * s).
-      // The constant's rounding error is below q_scale * k_scale / 2, i.e. under half a unit
-      // of the int32 dot product (whose INT8 quantization noise is far larger).
-      const float cst = fmaf(-kSeed, s, mneg);
-      float p[32];
+      // The code argument 8 x + kCodeOffset as ONE fma on the seeded pattern A = kSeed + score *
+      // 2^-26, with s = q_scale * k_scale * 2^26 in base-2 units: A * 8 s + (mneg - kSeed * 8 s).
+      // The constant's rounding error is below a tenth of a code step.
+      const float s8 = kCodeSlope * s;
+      const float cst = fmaf(-kSeed, s8, mneg);
+      float y[32];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[16 * tt + r] = fast_exp2(fmaf(__int_as_float(si[tt][r]), s, cst));
+        for (int r = 0; r < 16; ++r) y[16 * tt + r] = fmaf(__int_as_float(si[tt][r]), s8, cst);
       if (masked) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) p[16 * tt + r] = si[tt][r] == kMasked ? 0.0f : p[16 * tt + r];
+          for (int r = 0; r < 16; ++r) y[16 * tt + r] = si[tt][r] == kMasked ? -1.0f : y[16 * tt + r];
       }
-      // P (B operand, 32 e4m3 bytes): byte e = key 32 hl + e
+      // P (B operand, 32 e4m3 bytes): byte e = key 32 hl + e.  v_cvt_pk_u8_f32 rounds to the
+      // nearest integer and clamps to [0, 255]; y <= 8 * 8.8 + 56 - 0.35 < 126.5, so the largest
+      // code is 126 (448) and never 127 (NaN).  Every byte of the old word is overwritten.
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        // the low half is written here and the high half below: the old word's bits are discarded
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w], p[4 * w + 1], pf[w], false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * w + 2], p[4 * w + 3], word, true);
-        pf[w] = word;
+        uint32_t word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w], 0, (uint32_t)pf[w]);
+        word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 1], 1, word);
+        word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 2], 2, word);
+        word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 3], 3, word);
+        pf[w] = (int)word;
       }
       // keep the softmax in its phase: without the pin the compiler sinks the
-      // exponentials past the barrier, next to the P V products that consume them
+      // code conversions past the barrier, next to the P V products that consume them
       asm volatile("" : "+v"(pf));
     };
 
