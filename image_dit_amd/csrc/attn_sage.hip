@@ -46,9 +46,12 @@
 //   * P is stored as p * 2^8 in e4m3; the running max is raised lazily (only
 //     when a row's tile max exceeds it by more than 0.8 in base-2 units), so
 //     p * 2^8 <= 2^8.8 = 445.7 < 448.  The row sum l comes from one more FP8
-//     MFMA of an all-ones A operand with the same P: the matrix unit has slack
-//     here and the vector unit has none, and numerator and denominator then
-//     use the same rounded P.  O = acc * v_scale / l.
+//     MFMA with the same P: the matrix unit has slack here and the vector unit
+//     has none, and numerator and denominator then use the same rounded P.  It
+//     is a 16x16x128 product (half the cycles of a 32x32x64 one) that reads P in
+//     place as its B operand, with a constant 0 / 1 A operand that sums, for each
+//     output row block, the two lane groups holding one query's keys; every lane
+//     gets its own query's l (exact sums of e4m3 values).  O = acc * v_scale / l.
 //   * Two wave groups ping-pong on each SIMD (waves w and w + 4 share one):
 //     one group's matrix phase (K Q^T of this tile, then P V of the previous
 //     one, under which the new scores are masked and their row max taken) runs
@@ -175,18 +178,25 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
   auto masked_tile = [&](int t) __attribute__((always_inline)) { return t * BK < lo_last || t * BK + BK - 1 > hi_first; };
 
   f32x16 acc[4];  // O^T: channels 32 dt + (accumulator row), this lane's query
-  f32x16 lacc;    // row sums (every accumulator row holds this lane's query's l)
+  f32x4 lacc;     // row sum l of this lane's query (in each of the four)
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-  lacc = f32x16{};
+  lacc = f32x4{};
   float m = -INFINITY;
   // Kept with m (which changes only when the running max is raised): m + kLazyThresh, and the
   // code offset kCodeOffset + 8 (8 - m) (kCodeOffset while a row has no visible key, m = -inf).
   float m_thr = -INFINITY, mneg = kCodeOffset;
   const int unit_scale = unit_e8m0_scale();
-  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
-  asm volatile("" : "+v"(ones));  // kept in registers (else rebuilt before every row-sum MFMA)
+  // Row sums on one 16x16x128 FP8 MFMA that reads P in place as its B operand: lane L is then
+  // column L % 16 and holds 32 of the 128 k values, its k group L / 16 (the same grouping for A).
+  // Query q < 16 sits in lanes q (keys 0-31) and q + 32 (keys 32-63), k groups 0 and 2; query
+  // 16 + q in lanes 16 + q and 48 + q, groups 1 and 3.  Output row block i / 4 lands in lanes
+  // 16 (i / 4) .. + 15, whose query is q for even blocks and 16 + q for odd ones, so A row i is
+  // e4m3 1.0 on the k groups of the matching parity and 0 elsewhere: lane L of A (row L % 16,
+  // group L / 16) holds ones when (L / 16) % 2 == (L % 16 / 4) % 2.
+  const int rsel = ((l >> 4) & 1) == ((l >> 2) & 1) ? 0x38383838 : 0;
+  i32x8 lsel = {rsel, rsel, rsel, rsel, rsel, rsel, rsel, rsel};
+  asm volatile("" : "+v"(lsel));  // kept in registers (else rebuilt before every row-sum MFMA)
 
   if (n > 0) {
     // ---- global -> LDS (direct); every lane fetches the chunk that lands in its LDS slot.
@@ -315,7 +325,7 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
           __builtin_amdgcn_sched_barrier(0);
         };
         pv(J0{}); pv(J1{}); pv(J2{}); pv(J3{});
-        lacc = mfma_fp8_32x32x64(ones, pf, lacc, unit_scale);
+        lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lsel, pf, lacc, 0, 0, 0, unit_scale, 0, unit_scale);
       }
       if constexpr (QK) {
         if (masked_tile(t)) {

@@ -124,6 +124,7 @@ __device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b, u32x2& c, u32x2& d,
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(f32x4& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(i32x16& x) { asm volatile("" : "+v"(x)); }
 
 // Let the last MFMAs writing these accumulators retire before any VALU reads
@@ -136,6 +137,10 @@ __device__ __forceinline__ void mfma_drain(f32x16& a, f32x16& b, f32x16& c, f32x
 }
 
 __device__ __forceinline__ void mfma_drain(f32x16& a) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(a));
+}
+
+__device__ __forceinline__ void mfma_drain(f32x4& a) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" : "+v"(a));
 }
 
