@@ -53,9 +53,10 @@
 //     output row block, the two lane groups holding one query's keys; every lane
 //     gets its own query's l (exact sums of e4m3 values).  O = acc * v_scale / l.
 //   * Two wave groups ping-pong on each SIMD (waves w and w + 4 share one):
-//     one group's matrix phase (K Q^T of this tile, then P V of the previous
-//     one, under which the new scores are masked and their row max taken) runs
-//     under the other group's softmax.  Both phases are issue-bound: a single
+//     one group's matrix phase (the row sums of the previous tile's P while
+//     the first K fragments are read, K Q^T of this tile, then P V of the
+//     previous one) runs under the other group's softmax (mask and row max of
+//     the new scores, then the P codes).  Both phases are issue-bound: a single
 //     wave issues at most one vector instruction every few cycles and reads
 //     LDS at roughly 1 KB per 40 cycles, so each phase is bound by one wave's
 //     issue and LDS rates, not by the vector unit's width.  Only one wave per
@@ -245,13 +246,43 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
     i32x16 si[2];  // biased int32 scores of the latest tile, one 32-key sub-tile each
     i32x8 pf;      // P of the latest softmax (e4m3, p * 2^8)
     float s_tile;  // q_scale * k_scale * 2^26 of the half-wave's 32-key block in that tile
-    // ---- matrix phase: O^T += V^T P^T (and the row sums) for V stage VS (4 + 1 MFMA) and/or
-    // S^T = K Q^T for K stage KS (8 MFMA).
     float mx_tile;  // row max (scaled, log2 units) of the latest K Q^T, -inf where all hidden
     constexpr int kMasked = INT32_MIN;  // no real score gets there: |acc| <= 128 * 127^2
-    // ---- matrix phase: S^T = K Q^T for K stage KS (8 MFMA), then O^T += V^T P^T (and the
-    // row sums) for V stage VS (4 + 1 MFMA); under the P V products the new scores are
-    // masked (tiles crossing a mask boundary) and their row max taken.
+    // ---- mask and row max of the scores of tile t (in si), into mx_tile.  The plain kernel takes
+    // them at the start of the softmax phase (its matrix phase is the longer one); the split-tail
+    // kernel keeps them at the end of the matrix phase, as its work-item plan needs the registers
+    // the other placement takes.
+    auto row_max = [&](int t) __attribute__((always_inline)) {
+      if (masked_tile(t)) {
+        // keys t * BK + 32 hl + e, e = 16 tt + r, visible for e in [elo, ehi]
+        const int elo = lo_i - (t * BK + 32 * hl), ehi = hi_i - (t * BK + 32 * hl);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = 16 * tt + r;
+            si[tt][r] = (e < elo || e > ehi) ? kMasked : si[tt][r];
+          }
+      }
+      // row max on the biased int32 patterns (positive floats order like their bits), as a
+      // tree of v_max3_i32 for a short dependency chain
+      int m8[11];
+#pragma unroll
+      for (int j = 0; j < 10; ++j) {
+        const int e = 3 * j;
+        m8[j] = max(max(si[e >> 4][e & 15], si[(e + 1) >> 4][(e + 1) & 15]), si[(e + 2) >> 4][(e + 2) & 15]);
+      }
+      m8[10] = max(si[1][14], si[1][15]);
+      const int mi = max(max(max(max(m8[0], m8[1]), m8[2]), max(max(m8[3], m8[4]), m8[5])),
+                         max(max(max(m8[6], m8[7]), m8[8]), max(m8[9], m8[10])));
+      // s >= 0: scaling keeps the max; a half-wave with every key hidden contributes -inf
+      const float mh = mi == kMasked ? -INFINITY : (__int_as_float(mi) - kSeed) * s_tile;
+      mx_tile = half_pair_max_nc(mh);
+    };
+
+    // ---- matrix phase: the row sums of P (1 MFMA, first: it needs no LDS data), S^T = K Q^T
+    // for K stage KS (8 MFMA), then O^T += V^T P^T for V stage VS (4 MFMA).  The last matrix
+    // phase (P V only) takes the row sums after the P V products.
     auto mphase = [&](auto vs_c, auto ks_c, auto pv_c, auto qk_c, int t) __attribute__((always_inline)) {
       constexpr int VS = decltype(vs_c)::value, KS = decltype(ks_c)::value;
       constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
@@ -292,6 +323,9 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
         ksb = ds_read_b32<SB>(lds0 + 4 * hl);
         if constexpr (PV) {
           vread(J0{}); vread(J1{});
+          // the row sums need only P: they run while the first K fragment is on its way
+          lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lsel, pf, lacc, 0, 0, 0, unit_scale, 0, unit_scale);
+          __builtin_amdgcn_sched_barrier(0);
         }
         auto qk = [&](auto j_c) __attribute__((always_inline)) {
           constexpr int j = decltype(j_c)::value;
@@ -325,34 +359,13 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
           __builtin_amdgcn_sched_barrier(0);
         };
         pv(J0{}); pv(J1{}); pv(J2{}); pv(J3{});
-        lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lsel, pf, lacc, 0, 0, 0, unit_scale, 0, unit_scale);
+        // after the last tile the row sums come last: the epilogue reads the P V accumulators
+        // right after the drain, and this product keeps the matrix unit between the two
+        if constexpr (!QK)
+          lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lsel, pf, lacc, 0, 0, 0, unit_scale, 0, unit_scale);
       }
-      if constexpr (QK) {
-        if (masked_tile(t)) {
-          // keys t * BK + 32 hl + e, e = 16 tt + r, visible for e in [elo, ehi]
-          const int elo = lo_i - (t * BK + 32 * hl), ehi = hi_i - (t * BK + 32 * hl);
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int e = 16 * tt + r;
-              si[tt][r] = (e < elo || e > ehi) ? kMasked : si[tt][r];
-            }
-        }
-        // row max on the biased int32 patterns (positive floats order like their bits), as a
-        // tree of v_max3_i32 for a short dependency chain
-        int m8[11];
-#pragma unroll
-        for (int j = 0; j < 10; ++j) {
-          const int e = 3 * j;
-          m8[j] = max(max(si[e >> 4][e & 15], si[(e + 1) >> 4][(e + 1) & 15]), si[(e + 2) >> 4][(e + 2) & 15]);
-        }
-        m8[10] = max(si[1][14], si[1][15]);
-        const int mi = max(max(max(max(m8[0], m8[1]), m8[2]), max(max(m8[3], m8[4]), m8[5])),
-                           max(max(max(m8[6], m8[7]), m8[8]), max(m8[9], m8[10])));
-        // s >= 0: scaling keeps the max; a half-wave with every key hidden contributes -inf
-        const float mh = mi == kMasked ? -INFINITY : (__int_as_float(mi) - kSeed) * s_tile;
-        mx_tile = half_pair_max_nc(mh);
+      if constexpr (QK && SK) {
+        row_max(t);
         pin(si[0]);
         pin(si[1]);
         pin(mx_tile);
@@ -369,6 +382,7 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
     // accumulators); a tile crossing a mask boundary only takes two small branches: its
     // hidden scores become INT32_MIN before the row max, and their P codes become 0.
     auto softmax = [&](int t) __attribute__((always_inline)) {
+      if constexpr (!SK) row_max(t);
       const float s = s_tile;
       const bool masked = masked_tile(t);  // uniform
       const float mx = mx_tile;
@@ -505,6 +519,10 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
   }
 
   // ---- epilogue: O[i][d] = acc * v_scale[d] / l (0 for a row with no visible key)
+  // Twice the drain of a 16-pass MFMA: a partial piece stores these registers at once, and a
+  // single drain right after the last P V product let it store stale values (the split-tail
+  // test at 4608 x 1000 tokens with grouped heads then differed from run to run).
+  mfma_drain(acc[0], acc[1], acc[2], acc[3]);
   mfma_drain(acc[0], acc[1], acc[2], acc[3]);
   mfma_drain(lacc);
   float lsum = lacc[0];
