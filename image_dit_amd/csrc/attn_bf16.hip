@@ -429,7 +429,7 @@ __device__ __forceinline__ void attn_body(const Bf16Args& a) {
     return;
   }
   bool ok = true;
-  if (mode == kSplitOwner) ok = split_merge(a.ws_part, a.ws_flag, a.epoch, p_lo, p_hi, acc, m, lsum);
+  if (mode == kSplitOwner) ok = split_merge(a.ws_part, a.ws_flag, a.epoch, p_lo, p_hi, a.sk_tail_units, acc, m, lsum);
   // O = acc / l, BF16, rows < S_q (0 for a row with no visible key; NaN if a piece never came)
   const float lt = half_pair_sum(lsum);
   const float inv = !ok ? __builtin_nanf("") : (lt > 0.0f ? 1.0f / lt : 0.0f);

@@ -531,7 +531,7 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
     return;
   }
   bool ok = true;
-  if (mode == kSplitOwner) ok = split_merge(a.ws_part, a.ws_flag, a.epoch, p_lo, p_hi, acc, m, lsum);
+  if (mode == kSplitOwner) ok = split_merge(a.ws_part, a.ws_flag, a.epoch, p_lo, p_hi, a.sk_tail_units, acc, m, lsum);
   // (NaN if a piece never came)
   const float inv = !ok ? __builtin_nanf("") : (lsum > 0.0f ? 1.0f / lsum : 0.0f);
   if (qi < a.S_q) {

@@ -224,13 +224,17 @@ __device__ __forceinline__ void split_write_partial(float* part, uint32_t* flags
 }
 
 // Merge the partials of workgroups p_lo .. p_hi (lowest first) into this thread's (acc, m, l),
-// the blocked form's rescale by 2^(m_old - m_new); false when a piece never came.
+// the blocked form's rescale by 2^(m_old - m_new); false when a piece never came.  A workgroup
+// whose range of the tail_units units is empty (there are fewer units than workgroups) holds no
+// piece and is skipped.
 __device__ __forceinline__ bool split_merge(const float* part, const uint32_t* flags, uint32_t epoch, int p_lo,
-                                            int p_hi, f32x16 (&acc)[4], float& m, float& l) {
+                                            int p_hi, int64_t tail_units, f32x16 (&acc)[4], float& m, float& l) {
   __shared__ int ready_all;
   const int tid = threadIdx.x;
+  const int G = gridDim.x;
   bool ok = true;
   for (int g = p_lo; g <= p_hi; ++g) {
+    if (tail_units * g / G == tail_units * (g + 1) / G) continue;  // uniform
     if (tid == 0) ready_all = split_wait_flag(flags + g, epoch) ? 1 : 0;
     __syncthreads();
     ok = ok && ready_all != 0;
