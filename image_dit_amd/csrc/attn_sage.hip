@@ -55,8 +55,9 @@
 //   * Two wave groups ping-pong on each SIMD (waves w and w + 4 share one):
 //     one group's matrix phase (the row sums of the previous tile's P while
 //     the first K fragments are read, K Q^T of this tile, then P V of the
-//     previous one) runs under the other group's softmax (mask and row max of
-//     the new scores, then the P codes).  Both phases are issue-bound: a single
+//     previous one; the last phase takes the row sums after its P V) runs under
+//     the other group's softmax (mask and row max of the new scores, then the
+//     P codes).  Both phases are issue-bound: a single
 //     wave issues at most one vector instruction every few cycles and reads
 //     LDS at roughly 1 KB per 40 cycles, so each phase is bound by one wave's
 //     issue and LDS rates, not by the vector unit's width.  Only one wave per
@@ -66,6 +67,12 @@
 //     a query's window get p = 0.  Only tiles that cross a mask boundary for
 //     some row of the workgroup take the masked path; a row with no visible
 //     key writes zeros.
+//   * Split tail (sage_attn_fwd_split_kernel, entry point sage_attn_fwd_ws): the
+//     same body run over the work items of split_tail_items (common.hpp), one
+//     workgroup per CU, when the last round of query tiles is partial: pieces
+//     of a query tile leave FP32 (acc, m, l) partials that the piece holding
+//     the tile's last key tile merges.  It keeps the mask and row max at the end
+//     of the matrix phase (in the softmax phase they cost it 2 spilled VGPRs).
 #include <stdint.h>
 
 #include <type_traits>
