@@ -11,8 +11,8 @@ fallback.  Build it with `python -m image_dit_amd.build` (or
 `__graft_entry__.build()`).
 
 Pattern of the binding: "RDNAttention" README, sections "Overview" and
-"Quick start" -- read the device pointer out of existing tensors and call the
-kernel on it, with no staging copies and no second GPU context.
+"Quick start" -- the kernels get the addresses of tensors that already live on
+the GPU; nothing is copied and no GPU context of the binding's own is opened.
 """
 import ctypes
 import os

@@ -17,9 +17,10 @@
  *          sections "Technical Details" and the two commit messages: the
  *          prepare stage and the quantized forward, non-causal, head dim 128,
  *          no mask or varlen, BF16 in and out, forward only.
- *   [RDNA] "RDNAttention" README, sections "Overview" and "Quick start": a
- *          thin wrapper that hands the device pointers of existing tensors to
- *          the kernel, with no staging copies and no second GPU context.
+ *   [RDNA] "RDNAttention" README, sections "Overview" and "Quick start": the
+ *          layer above the kernels only passes the addresses of tensors that
+ *          already live on the GPU; it copies nothing and opens no GPU context
+ *          of its own.
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers owned by the caller.  The library
@@ -230,14 +231,17 @@ int sage_prepare_ex_noalloc(const void* q, const void* k, const void* v, int8_t*
  *                    zero-filled once before first use is recommended); may be NULL
  *                    when that size is 0
  *   workspace_bytes  its size; too small -> DITATTN_EINVAL before anything is enqueued
- * When the size is 0 (key window on, fewer query tiles than compute units, or a last
- * round that already fills the GPU) the call is attn_fwd_bf16_ex.  Otherwise the grid is
- * one workgroup per compute unit: whole query tiles first, then equal ranges of (query
- * tile, key tile) units; a query tile split over several workgroups is merged, in a
- * fixed order, by the one holding its last key tile from FP32 partials (m, l, O) the
- * others leave in the workspace.  The result meets the same accuracy as attn_fwd_bf16_ex's
- * (it differs from it by the rounding of P to BF16, taken relative to each piece's own
- * running max) and is run-to-run deterministic.  One workspace serves one call at a time.
+ * When the size is 0 (key window on, fewer than three whole rounds of query tiles, one
+ * key tile per query tile, or a last round that is already 95 % full) the call is
+ * attn_fwd_bf16_ex.  Otherwise the grid is one workgroup per compute unit: whole query
+ * tiles first, then equal ranges of (query tile, key tile) units; a query tile split over
+ * several workgroups is merged, in a fixed order, by the one holding its last key tile
+ * from FP32 partials (m, l, O) the others leave in the workspace.  The result meets the
+ * same accuracy as attn_fwd_bf16_ex's (it differs from it by the rounding of P to BF16,
+ * taken relative to each piece's own running max) and is run-to-run deterministic.  One
+ * workspace serves one call at a time.  A workgroup waits for another's partial for at
+ * most about a second (the whole grid is resident, so it does not wait that long); a
+ * partial that never comes leaves its rows NaN instead of hanging the GPU.
  */
 int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int B, int S_q,
                      int S_kv, int H, int H_kv, int D, float scale, int window_left,
@@ -304,12 +308,14 @@ int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
  *                    zero-filled once before first use is recommended); may be NULL
  *                    when that size is 0
  *   workspace_bytes  its size; too small -> DITATTN_EINVAL before anything is enqueued
- * When the size is 0 (key window on, fewer than three rounds of query tiles, or a last
- * round that already fills the GPU) the call is sage_attn_fwd_ex.  Otherwise a query tile
- * split over several workgroups is merged, in a fixed order, from FP32 partials (m, l, acc)
- * by the workgroup holding its last key tile.  The result meets sage_attn_fwd_ex's accuracy
- * (it differs from it by P's FP8 rounding, taken relative to each piece's own running max)
- * and is run-to-run deterministic.  One workspace serves one call at a time.
+ * When the size is 0 (key window on, fewer than three whole rounds of query tiles, one
+ * key tile per query tile, or a last round that is already 95 % full) the call is
+ * sage_attn_fwd_ex.  Otherwise a query tile split over several workgroups is merged, in a
+ * fixed order, from FP32 partials (m, l, acc) by the workgroup holding its last key tile.
+ * The result meets sage_attn_fwd_ex's accuracy (it differs from it by P's FP8 rounding,
+ * taken relative to each piece's own running max) and is run-to-run deterministic.  One
+ * workspace serves one call at a time.  Waits for partials are bounded as in
+ * attn_fwd_bf16_ws (NaN rows instead of a hang).
  */
 int sage_attn_fwd_ws(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                      const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
