@@ -14,6 +14,11 @@ The same JSON line carries one row per (workload, mode) for the DiT shapes:
   sage_core  sage_attn_fwd_ws on prepared tensors (the plain sage_attn_fwd kernel
              unless the last round of query tiles is split)   vs the 8-bit MFMA peak
   prepare    sage_prepare                       vs the HBM peak (algorithmic bytes)
+and rows of the path's variants, on a base workload's tensors (the _ws entry points):
+  bf16_X, sage_core_X   X = causal (key window (-1, 0)), gqa4 (H_kv = H / 4), text512
+                        (cross-attention to 512 tokens); TFLOPS count the visible pairs only
+  prepare_xform         sage_prepare_ex with RMSNorm + RoPE (rope_dim 128) fused
+  prepare_smoothk       sage_prepare_ex with K smoothing (one more read of K)
 Rows are timed first, each for at least --row-ms milliseconds, and the headline
 follows the last one with no idle gap (its inputs are made beforehand): the
 shader clock drops within a fraction of a second of idling and takes longer
@@ -47,11 +52,30 @@ KERNEL_SOURCES = {
     "sage_attn_fwd": ["image_dit_amd/csrc/attn_sage.hip", "image_dit_amd/csrc/common.hpp"],
     "sage_prepare": ["image_dit_amd/csrc/prepare.hip", "image_dit_amd/csrc/common.hpp"],
 }
-MODES = ("bf16", "sage", "sage_core", "prepare")
+# Variants of the path (cross-attention to text tokens, grouped heads, a causal key window,
+# the fused Q/K transform and K smoothing in prepare), each on a base workload's tensors:
+# attention variants count only the visible (query, key) pairs, prepare variants their own bytes.
+VARIANTS = {
+    "causal": dict(window=(-1, 0)),   # bottom-right aligned: query i sees keys 0..i
+    "gqa4": dict(hkv_div=4),          # H_kv = H / 4 (the first H / 4 heads of K and V)
+    "text512": dict(s_kv=512),        # cross-attention to 512 tokens (the first 512 of K and V)
+}
+PREP_VARIANTS = {
+    "xform": dict(rope_dim=128),      # RMSNorm (seeded weights) + rotate-half RoPE on all 128 channels
+    "smoothk": dict(smooth_k=True),   # K's channel mean subtracted before INT8
+}
+MODES = (("bf16", "sage", "sage_core", "prepare")
+         + tuple("%s_%s" % (m, v) for v in VARIANTS for m in ("bf16", "sage_core"))
+         + tuple("prepare_%s" % v for v in PREP_VARIANTS))
 # largest first; the FLUX-1024 rows last, right before the headline at that shape
 DEFAULT_ROWS = ["wan720p:bf16", "wan720p:sage", "wan720p:sage_core", "wan720p:prepare",
                 "flux2048:bf16", "flux2048:sage", "flux2048:sage_core", "flux2048:prepare",
                 "hunyuan720p:bf16", "hunyuan720p:sage", "hunyuan720p:sage_core", "hunyuan720p:prepare",
+                "wan720p:bf16_text512", "wan720p:sage_core_text512", "wan720p:prepare_xform",
+                "wan720p:prepare_smoothk",
+                "flux2048:bf16_causal", "flux2048:sage_core_causal", "flux2048:bf16_gqa4",
+                "flux2048:sage_core_gqa4",
+                "flux1024:prepare_xform", "flux1024:prepare_smoothk",
                 "flux1024:prepare", "flux1024:sage_core", "flux1024:sage"]
 
 
@@ -212,6 +236,7 @@ class Inputs:
         self.q, self.k, self.v = (t.to(dev) for t in qkv)
         self.out = torch.empty_like(self.q)
         self._prep = None
+        self._var, self._pvar = {}, {}
         import image_dit_amd as ia
         # the BF16 and Sage rows run the _ws entry points: the last, partial round of query tiles
         # is split over every CU where that pays (workspace size > 0), else they are the plain
@@ -225,6 +250,50 @@ class Inputs:
         if self._prep is None:
             self._prep = ia.sage_prepare(self.q, self.k, self.v, self.w.scale, stream=stream)
         return self._prep
+
+    def variant(self, name, stream):
+        """Tensors of an attention variant: (k, v, prepared, window, H_kv, S_kv, workspace)."""
+        import torch
+        import image_dit_amd as ia
+        if name not in self._var:
+            spec, w = VARIANTS[name], self.w
+            window = spec.get("window", (-1, -1))
+            H_kv = w.H // spec.get("hkv_div", 1)
+            S_kv = spec.get("s_kv", w.S)
+            if H_kv == w.H and S_kv == w.S:
+                k, v, prep = self.k, self.v, self.prepared(stream)
+            else:
+                k = self.k[:, :S_kv, :H_kv].contiguous()
+                v = self.v[:, :S_kv, :H_kv].contiguous()
+                prep = ia.sage_prepare_ex(self.q, k, v, w.scale, stream=stream)
+            nb = max(ia.bf16_workspace_size(w.B, w.S, S_kv, w.H, H_kv, window),
+                     ia.sage_attn_workspace_size(w.B, w.S, S_kv, w.H, H_kv, window))
+            ws = torch.zeros(nb, dtype=torch.uint8, device=self.q.device) if nb else None
+            self._var[name] = (k, v, prep, window, H_kv, S_kv, ws)
+        return self._var[name]
+
+    def prep_variant(self, name):
+        """Arguments of a prepare variant (and its own outputs, so the base prepared tensors
+        stay as they are)."""
+        import torch
+        import image_dit_amd as ia
+        from image_dit_amd import synth
+        if name not in self._pvar:
+            spec, w, dev = PREP_VARIANTS[name], self.w, self.q.device
+            kw = {}
+            if spec.get("rope_dim"):
+                cos, sin = synth.make_rope_tables(w.S, spec["rope_dim"])
+                kw.update(q_norm_w=synth.make_norm_weight(seed=1).to(dev),
+                          k_norm_w=synth.make_norm_weight(seed=2).to(dev),
+                          rope_cos=cos.to(dev), rope_sin=sin.to(dev), rope_dim=spec["rope_dim"])
+            if spec.get("smooth_k"):
+                nb = ia.sage_workspace_size(w.B, w.S, w.H)
+                kw.update(smooth_k=True, k_mean=torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev),
+                          workspace=torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
+            specs = ia._prepared_specs(w.B, w.S, w.H, w.D, w.S, w.H)
+            kw["out"] = tuple(torch.empty(shape, dtype=dt, device=dev) for _, shape, dt in specs)
+            self._pvar[name] = kw
+        return self._pvar[name]
 
 
 def mode_fn(inp, mode, stream):
@@ -245,6 +314,20 @@ def mode_fn(inp, mode, stream):
             ia.sage_attn_fwd_ws(prep, w.S, w.S, w.H, w.H, w.scale, out=inp.out, workspace=inp.ws,
                                 stream=stream)
         return f
+    base, _, var = mode.partition("_")
+    if mode.startswith("sage_core_"):
+        base, var = "sage_core", mode[len("sage_core_"):]
+    if base == "prepare" and var in PREP_VARIANTS:
+        kw = inp.prep_variant(var)
+        return lambda: ia.sage_prepare_ex(inp.q, inp.k, inp.v, w.scale, stream=stream, **kw)
+    if var in VARIANTS:
+        k, v, vprep, window, H_kv, S_kv, ws = inp.variant(var, stream)
+        if base == "bf16":
+            return lambda: ia.attn_fwd_bf16_ws(inp.q, k, v, w.scale, window=window, out=inp.out, workspace=ws,
+                                               stream=stream)
+        if base == "sage_core":
+            return lambda: ia.sage_attn_fwd_ws(vprep, w.S, S_kv, w.H, H_kv, w.scale, window=window, out=inp.out,
+                                               workspace=ws, stream=stream)
     raise ValueError(mode)
 
 
@@ -252,6 +335,21 @@ def row_record(w, mode, ms, reps):
     from image_dit_amd import cost
     flops = cost.attn_flops(w.B, w.H, w.S, w.D)
     rec = {"workload": w.name, "mode": mode, "B": w.B, "H": w.H, "S": w.S, "ms": ms, "reps": reps}
+    var = mode.rsplit("_", 1)[-1] if "_" in mode and mode != "sage_core" else ""
+    if var in VARIANTS:
+        spec = VARIANTS[var]
+        window = spec.get("window", (-1, -1))
+        H_kv, S_kv = w.H // spec.get("hkv_div", 1), spec.get("s_kv", w.S)
+        flops = cost.attn_flops_ex(w.B, w.H, w.S, S_kv, w.D, window)
+        rec.update(S_kv=S_kv, H_kv=H_kv, window=list(window), flop=flops)
+    if mode.startswith("prepare_"):
+        spec = PREP_VARIANTS[var]
+        nbytes = cost.sage_prepare_bytes_ex(w.B, w.H, w.S, w.S, w.H, w.D, rope_dim=spec.get("rope_dim", 0),
+                                            smooth_k=spec.get("smooth_k", False))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rec.update(bound="hbm", gbs=gbs, algorithmic_bytes=nbytes, peak=PEAK_HBM_GBS,
+                   frac=gbs / PEAK_HBM_GBS)
+        return rec
     if mode == "prepare":
         nbytes = cost.sage_prepare_bytes(w.B, w.H, w.S, w.D)
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -259,7 +357,7 @@ def row_record(w, mode, ms, reps):
                    frac=gbs / PEAK_HBM_GBS)
     else:
         tf = flops / (ms * 1e-3) / 1e12
-        peak = PEAK_TFLOPS["bf16" if mode == "bf16" else "int8"]
+        peak = PEAK_TFLOPS["bf16" if mode.startswith("bf16") else "int8"]
         rec.update(bound="mfma", tflops=tf, peak=peak, frac=tf / peak)
     return rec
 

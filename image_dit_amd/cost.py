@@ -49,3 +49,40 @@ def sage_attn_bytes(B: int, H: int, S: int, D: int = 128) -> float:
     Sp = sage_padded_len(S)
     read = 3.0 * B * H * Sp * D + 4.0 * (2 * B * H * (Sp // 32) + B * H * D)
     return read + 2.0 * B * S * H * D
+
+
+def visible_pairs(S_q: int, S_kv: int, window=(-1, -1)) -> int:
+    """(query, key) pairs a key window leaves visible in one (b, h): query i sees key j when
+    i + off - wl <= j <= i + off + wr with off = S_kv - S_q (a negative bound: none)."""
+    wl, wr = window
+    if wl < 0 and wr < 0:
+        return S_q * S_kv
+    import numpy as np
+    i = np.arange(S_q, dtype=np.int64) + (S_kv - S_q)
+    lo = np.zeros_like(i) if wl < 0 else np.maximum(i - wl, 0)
+    hi = np.full_like(i, S_kv - 1) if wr < 0 else np.minimum(i + wr, S_kv - 1)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def attn_flops_ex(B: int, H: int, S_q: int, S_kv: int, D: int = 128, window=(-1, -1)) -> float:
+    """4 * D FLOPs per visible (query, key) pair: cross-attention, grouped heads (which do not
+    change the count) and key windows, whose hidden pairs are not counted."""
+    return 4.0 * B * H * D * visible_pairs(S_q, S_kv, window)
+
+
+def sage_prepare_bytes_ex(B: int, H: int, S_q: int, S_kv: int, H_kv: int, D: int = 128, rope_dim: int = 0,
+                          smooth_k: bool = False) -> float:
+    """sage_prepare_bytes for cross-attention / grouped-head shapes, plus the RMSNorm weights
+    and RoPE tables of the fused transform (two [max(S_q, S_kv), rope_dim] BF16 tables) and,
+    with K smoothing, one more read of K (its channel mean must be known before K is
+    quantized) and the mean's write."""
+    Spq, Spk = sage_padded_len(S_q), sage_padded_len(S_kv)
+    read = 2.0 * (B * S_q * H * D + 3 * B * S_kv * H_kv * D)  # Q, K, V and V again
+    write = (B * H * Spq * D + 2.0 * B * H_kv * Spk * D
+             + 4.0 * (B * H * (Spq // 32) + B * H_kv * (Spk // 32) + B * H_kv * D))
+    if rope_dim:
+        read += 2.0 * 2 * max(S_q, S_kv) * rope_dim + 2.0 * 2 * D
+    if smooth_k:
+        read += 2.0 * B * S_kv * H_kv * D
+        write += 4.0 * B * H_kv * D
+    return read + write
