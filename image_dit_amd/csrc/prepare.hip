@@ -259,7 +259,7 @@ xform_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ out, int S, 
 // Per-(b, h, channel) mean of the (transformed) K values over the S tokens:
 // mean = fp32(fp64 sum / S).  k_colsum_kernel writes fp64 partial sums per token
 // range (no atomics, fixed order) to the workspace [B, nchunk, H, 128]; k_mean_kernel
-// adds them in range order.  Both sums are exact, hence order free, whenever the
+// adds them up in a fixed order.  Both sums are exact, hence order free, whenever the
 // values of a channel span less than 2^(45 - log2 S) in magnitude.
 // Grid and lanes as v_absmax_kernel: a workgroup covers 4 heads (64 lanes x 16 B) of
 // one token range; the 16 lanes of one head row sit together, as the transform needs.
@@ -304,18 +304,33 @@ k_colsum_kernel(const uint16_t* __restrict__ k, double* __restrict__ partial, in
   }
 }
 
-// grid: ceil(B * H * 128 / 256); one thread per (b, h, channel).
+// grid: ceil(B * H * 128 / 16) workgroups of 256 threads, 16 consecutive (b, h, channel)
+// outputs each (so a load instruction reads 16 full 128-B lines): thread t adds the ranges
+// t / 16, t / 16 + 16, ... of output t % 16, then the 16 sums of an output are added in a
+// fixed order.  A single thread walking all ranges waits out one dependent load per range
+// (about 150 of them at 4608 tokens); the sums are exact, so their order is free.
 __global__ void __launch_bounds__(256)
 k_mean_kernel(const double* __restrict__ partial, float* __restrict__ k_mean, int S, int H,
               int nchunk, int n) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n) return;
-  const int hc = H * kHeadDim;
-  const int b = idx / hc, r = idx - b * hc;
-  const double* p = partial + (int64_t)b * nchunk * hc + r;
+  __shared__ double red[16][17];
+  const int o = threadIdx.x & 15, cl = threadIdx.x >> 4;
+  const int idx = blockIdx.x * 16 + o;
   double s = 0.0;
-  for (int c = 0; c < nchunk; ++c) s += p[(int64_t)c * hc];
-  k_mean[idx] = (float)(s / (double)S);
+  if (idx < n) {
+    const int hc = H * kHeadDim;
+    const int b = idx / hc, r = idx - b * hc;
+    const double* p = partial + (int64_t)b * nchunk * hc + r;
+#pragma unroll 4
+    for (int c = cl; c < nchunk; c += 16) s += p[(int64_t)c * hc];
+  }
+  red[cl][o] = s;
+  __syncthreads();
+  if (cl == 0 && idx < n) {
+    double t = 0.0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) t += red[c][o];
+    k_mean[idx] = (float)(t / (double)S);
+  }
 }
 
 // ---------------------------------------------------------------- V absmax
@@ -511,7 +526,7 @@ hipError_t launch_sage_prepare(const PrepareArgs& a, hipStream_t stream) {
                     a.S_kv, a.H_kv, ch.tok_per_wg, ch.nchunk, ch.colblk, kx);
     if (e != hipSuccess) return e;
     const int n = a.B * a.H_kv * kHeadDim;
-    e = launch(prep::k_mean_kernel, dim3((n + 255) / 256), dim3(256), stream, (const double*)partial,
+    e = launch(prep::k_mean_kernel, dim3((n + 15) / 16), dim3(256), stream, (const double*)partial,
                a.k_mean, a.S_kv, a.H_kv, ch.nchunk, n);
     if (e != hipSuccess) return e;
   }
