@@ -247,7 +247,8 @@ def bf16_workspace_size(B, S_q, S_kv, H, H_kv, window=(-1, -1)):
 def attn_fwd_bf16_ws(q, k, v, scale, window=(-1, -1), out=None, workspace=None, stream=None):
     """attn_fwd_bf16_ex with a workspace that splits the last, partial round of query
     tiles over every compute unit (see bf16_workspace_size).  workspace: a contiguous
-    device buffer of at least that many bytes, allocated (zero-filled) here when None.
+    device buffer of at least that many bytes, zero-filled before its first use
+    (allocated zero-filled here when None).
     One workspace serves one call at a time."""
     import torch
     lib = load()
@@ -506,7 +507,8 @@ def sage_attn_fwd_ws(prepared, S_q, S_kv, H, H_kv, scale, window=(-1, -1), out=N
                      stream=None):
     """sage_attn_fwd_ex with a workspace that splits the last, partial round of query tiles
     over every compute unit (see sage_attn_workspace_size).  workspace: a contiguous buffer
-    on the tensors' GPU of at least that many bytes, allocated (zero-filled) here when None.
+    on the tensors' GPU of at least that many bytes, zero-filled before its first use
+    (allocated zero-filled here when None).
     One workspace serves one call at a time."""
     import torch
     lib = load()

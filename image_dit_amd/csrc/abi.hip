@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <chrono>
 
 #include "../../include/ditattn.h"
 #include "launch.hpp"
@@ -74,8 +75,18 @@ int check_xform(const void* norm_w0, const void* norm_w1, float eps, const void*
 float log2e_scale(float scale) { return static_cast<float>(static_cast<double>(scale) * kLog2eD); }
 
 // Per-call token of the split-tail flags: a flag counts as raised only when it holds this
-// call's value, so the workspace needs no clearing between calls.
-std::atomic<uint32_t> g_epoch{0};
+// call's value, so the workspace needs no clearing between calls.  The numbering starts at a
+// point drawn once per process (clock and address bits through a 64-bit mix), so flags a
+// workspace still holds from another process's calls do not match this process's tokens.
+uint32_t epoch_base() {
+  uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  x ^= (uint64_t)(uintptr_t)&x;  // stack address: differs between processes
+  x += 0x9E3779B97F4A7C15ull;    // splitmix64 finalizer
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return (uint32_t)(x ^ (x >> 31));
+}
+std::atomic<uint32_t> g_epoch{epoch_base()};
 uint32_t next_epoch() {
   uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
   if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
