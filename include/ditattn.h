@@ -239,9 +239,11 @@ int sage_prepare_ex_noalloc(const void* q, const void* k, const void* v, int8_t*
  * from FP32 partials (m, l, O) the others leave in the workspace.  The result meets the
  * same accuracy as attn_fwd_bf16_ex's (it differs from it by the rounding of P to BF16,
  * taken relative to each piece's own running max) and is run-to-run deterministic.  One
- * workspace serves one call at a time.  A workgroup waits for another's partial for at
- * most about a second (the whole grid is resident, so it does not wait that long); a
- * partial that never comes leaves its rows NaN instead of hanging the GPU.
+ * workspace serves one call at a time.  A workgroup waits only for partials of lower-numbered
+ * workgroups, and for at most about a second: with the GPU to itself the whole grid (one
+ * workgroup per compute unit) is resident and the waits are short; kernels running at the
+ * same time on other streams can hold compute units and delay the pieces, and a partial that
+ * does not come within the bound leaves its rows NaN instead of hanging the GPU.
  */
 int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int B, int S_q,
                      int S_kv, int H, int H_kv, int D, float scale, int window_left,
