@@ -18,7 +18,10 @@ Citations (page title, section):
     transposed to [B, H, 128, S_pad]);
   * Q/K row transform: the same page, first commit and "Technical Details"
     (optional RMSNorm and rotate-half RoPE, rope_dim 32/64/96/128, rounded like
-    the eager PyTorch BF16 sequence).
+    the eager PyTorch BF16 sequence);
+  * attention of the quantized operands: the same page, commit text of
+    gfx1201_sage_attention (INT8 Q K^T, FP8 P V, FP32 scales, online softmax in
+    base 2), exact in fp64, without the rounding of P.
 """
 import ctypes
 import math
@@ -65,9 +68,12 @@ def _lib():
         lib.oracle_f32_to_bf16.argtypes = [cf]
         lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
         lib.oracle_qk_norm_rope.argtypes = [u16p, ci, ci, ci, ci, u16p, cf, u16p, u16p, ci, u16p]
+        lib.oracle_sage_attn_rows.argtypes = [i8p, f32p, i8p, f32p, u8p, f32p, ci, ci, ci, ci, ci,
+                                              i64p, ctypes.c_int64, f64p, ci]
         for name in ("oracle_softmax_row", "oracle_attn_rows", "oracle_attn_blocked",
                      "oracle_quant_qk", "oracle_quant_v", "oracle_qk_norm_rope",
-                     "oracle_quant_qk_mean", "oracle_channel_mean", "oracle_attn_rows_ex"):
+                     "oracle_quant_qk_mean", "oracle_channel_mean", "oracle_attn_rows_ex",
+                     "oracle_sage_attn_rows"):
             getattr(lib, name).restype = ci
         _LIB = lib
     return _LIB
@@ -237,6 +243,29 @@ def sage_prepare(q, k, v, scale):
     kc, ks = quant_qk(k, 1.0)
     vc, vs = quant_v(v)
     return qc, qs, kc, ks, vc, vs
+
+
+def sage_attn_rows(prepared, S, rows, nthreads=0):
+    """Attention of the quantized operands (q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale) as
+    sage_prepare returns them, exact in fp64, for S real tokens and the query rows `rows`
+    (n x 3 array of b, h, i): the scores are the INT8 dot products times both block scales, in
+    base 2 (Q's scale carries softmax_scale * log2(e)); P V uses the decoded FP8 V times its
+    channel scale.  Returns [n, D]."""
+    qc, qs, kc, ks, vc, vs = (np.ascontiguousarray(a) for a in prepared)
+    B, H, S_pad, D = qc.shape
+    assert qc.dtype == np.int8 and kc.dtype == np.int8 and vc.dtype == np.uint8
+    assert qs.dtype == np.float32 and ks.dtype == np.float32 and vs.dtype == np.float32
+    assert kc.shape == qc.shape and vc.shape == (B, H, D, S_pad) and vs.shape == (B, H, D)
+    assert qs.shape == ks.shape == (B, H, S_pad // 32) and 0 < S <= S_pad
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], D), dtype=np.float64)
+    _check(_lib().oracle_sage_attn_rows(_ptr(qc, ctypes.c_int8), _ptr(qs, ctypes.c_float),
+                                        _ptr(kc, ctypes.c_int8), _ptr(ks, ctypes.c_float),
+                                        _ptr(vc, ctypes.c_uint8), _ptr(vs, ctypes.c_float),
+                                        B, S, H, D, S_pad, _ptr(rows, ctypes.c_int64),
+                                        rows.shape[0], _ptr(out, ctypes.c_double), nthreads),
+           "oracle_sage_attn_rows")
+    return out
 
 
 def f32_to_bf16(x):

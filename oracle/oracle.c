@@ -63,6 +63,13 @@
  *         an fp32 operation rounded to BF16 (round to nearest even), which is
  *         how eager PyTorch evaluates BF16 tensor arithmetic.
  *       - RMSNorm (when enabled) comes first, then RoPE, then the quantizer.
+ *  4. Attention of the quantized operands, in fp64 (same page, commit text of
+ *     gfx1201_sage_attention: Q K^T on the INT8 codes, P V on the FP8 V codes,
+ *     FP32 scales, online softmax; Q's scale carries softmax_scale * log2(e),
+ *     so the softmax is taken in base 2).  It is what the Sage attention
+ *     computes when only its inputs are rounded: its distance to (1) is the
+ *     quantizer's error, a kernel's distance to it is the kernel's own
+ *     (chiefly the rounding of P to FP8).
  *
  * Inputs are BF16 bit patterns (uint16) in [B, S, H, D] order.  Build with
  * plain gcc, -O2 -ffp-contract=off, no fast-math: the quantizer must round
@@ -571,6 +578,74 @@ int oracle_attn_rows_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
           out[r * D + d] += (s[j] / l) * (double)bf16_to_f32(v[((b * S_kv + j) * H_kv + hk) * D + d]);
     }
     free(s);
+  }
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 4. Attention of the quantized operands                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For each row (b, h, i) of rows (nrows triples), with the codes and scales in
+ * the layouts oracle_quant_qk and oracle_quant_v write (S real tokens of S_pad):
+ *   x_j = (sum_d qc[b,h,i,d] * kc[b,h,j,d]) * qs[b,h,i/32] * ks[b,h,j/32],  j < S
+ *   p_j = 2^(x_j - max_j x_j)
+ *   out[r][d] = vs[b,h,d] * (sum_j p_j * e4m3(vc[b,h,d,j])) / (sum_j p_j)
+ * The dot products of codes are exact integers; the rest is fp64.
+ */
+int oracle_sage_attn_rows(const int8_t* qc, const float* qs, const int8_t* kc, const float* ks,
+                          const uint8_t* vc, const float* vs, int B, int S, int H, int D,
+                          int S_pad, const int64_t* rows, int64_t nrows, double* out,
+                          int nthreads) {
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || S_pad < S || S_pad % 32 != 0 || nrows < 0)
+    return ORACLE_EINVAL;
+  for (int64_t r = 0; r < nrows; ++r) {
+    if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= H ||
+        rows[3 * r + 2] < 0 || rows[3 * r + 2] >= S)
+      return ORACLE_EINVAL;
+  }
+#ifdef _OPENMP
+  const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();  /* this call only */
+#else
+  (void)nthreads;
+#endif
+  int status = ORACLE_OK;
+#pragma omp parallel num_threads(nt)
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!x) {
+#pragma omp atomic write
+      status = ORACLE_ENOMEM;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (!x) continue;
+      const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+      const int64_t bh = b * H + h;
+      const int8_t* qrow = qc + (bh * S_pad + i) * D;
+      const double q_s = (double)qs[bh * (S_pad / 32) + i / 32];
+      double xmax = -INFINITY;
+      for (int j = 0; j < S; ++j) {
+        const int8_t* krow = kc + (bh * S_pad + j) * D;
+        int64_t dot = 0;
+        for (int d = 0; d < D; ++d) dot += (int64_t)qrow[d] * (int64_t)krow[d];
+        x[j] = (double)dot * q_s * (double)ks[bh * (S_pad / 32) + j / 32];
+        if (x[j] > xmax) xmax = x[j];
+      }
+      double l = 0.0;
+      for (int j = 0; j < S; ++j) {
+        x[j] = exp2(x[j] - xmax);
+        l += x[j];
+      }
+      for (int d = 0; d < D; ++d) {
+        const uint8_t* vrow = vc + (bh * D + d) * S_pad;
+        double acc = 0.0;
+        for (int j = 0; j < S; ++j) acc += x[j] * oracle_e4m3_decode(vrow[j]);
+        out[r * D + d] = (double)vs[bh * D + d] * acc / l;
+      }
+    }
+    free(x);
   }
   return status;
 }

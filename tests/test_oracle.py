@@ -7,7 +7,9 @@ form, and PyTorch's scaled_dot_product_attention in float64 as an independent
 library routine.  The quantizer ("gfx1201_sage_prepare /
 gfx1201_sage_attention", section "Technical Details") is pinned by hand-made
 blocks with known codes, the OCP E4M3 value table and torch's float8_e4m3fn
-conversion.
+conversion.  Attention of the quantized operands (same page, commit text of the
+attention op) is pinned to exact attention on inputs the quantizer represents
+exactly, and by its closed forms at one key and at equal scores.
 """
 import math
 
@@ -578,3 +580,87 @@ def test_thread_count_of_one_call_does_not_stick():
     assert oracle.num_threads() == before
     assert np.array_equal(a, oracle.attn_rows(q, k, v, SCALE, rows=rows))
     assert np.array_equal(b, oracle.attn_rows_ex(q, k, v, SCALE, (-1, 0), rows=rows))
+
+
+# --------------------------------------------------------------------------
+# attention of the quantized operands
+# --------------------------------------------------------------------------
+
+def exactly_quantizable(B, S, H, seed, D=128):
+    """BF16 Q, K, V that the quantizer represents exactly: each 32-row Q/K block holds integers
+    c in [-127, 127] (one of them +-127) times its own power of two, and each V channel holds
+    E4M3 values (one of them +-448) times its own power of two."""
+    g = np.random.default_rng(seed)
+    nblk = -(-S // 32)
+
+    def qk():
+        c = g.integers(-127, 128, size=(B, S, H, D))
+        e = g.integers(-7, -4, size=(B, nblk, H))          # 2^-7 .. 2^-5 per block
+        for b in range(B):
+            for blk in range(nblk):
+                for h in range(H):
+                    c[b, 32 * blk + g.integers(0, min(32, S - 32 * blk)), h, g.integers(0, D)] = \
+                        127 * (1 if g.random() < 0.5 else -1)
+        return c * np.exp2(np.repeat(e, 32, axis=1)[:, :S, :, None])
+
+    mags = np.array([oracle.e4m3_decode(cd) for cd in range(127)])
+    vm = mags[g.integers(0, 127, size=(B, S, H, D))] * np.where(g.random((B, S, H, D)) < 0.5, 1, -1)
+    for b in range(B):
+        for h in range(H):
+            for d in range(D):
+                vm[b, g.integers(0, S), h, d] = 448.0
+    ev = g.integers(-10, -5, size=(B, 1, H, D))             # 2^-10 .. 2^-6 per channel
+    v = vm * np.exp2(ev)
+    return tuple(bf16(x) for x in (qk(), qk(), v))
+
+
+@pytest.mark.parametrize("B,S,H", [(1, 64, 1), (2, 100, 3)])
+def test_sage_attn_rows_is_exact_attention_on_exact_codes(B, S, H):
+    # On inputs the quantizer represents exactly, attention of the quantized operands is exact
+    # attention up to the fp32 rounding of Q's multiplier (relative 2^-23 per score); a wrong
+    # scale block, V transpose, V channel scale or base of the softmax fails by far more.
+    q, k, v = exactly_quantizable(B, S, H, seed=B * 1000 + S)
+    prep = oracle.sage_prepare(q, k, v, SCALE)
+    qc, qs, kc, ks, vc, vs = prep
+    # the premise: codes times scales give back the inputs (Q times its multiplier)
+    mult = oracle.q_multiplier(SCALE)
+    kd = kc[:, :, :S].astype(np.float64) * np.repeat(ks, 32, axis=2)[:, :, :S, None]
+    assert np.array_equal(kd, f64(k).transpose(0, 2, 1, 3))
+    qd = qc[:, :, :S].astype(np.float64) * np.repeat(qs, 32, axis=2)[:, :, :S, None]
+    np.testing.assert_allclose(qd, f64(q).transpose(0, 2, 1, 3) * mult, rtol=2e-7, atol=0)
+    dec = np.array([oracle.e4m3_decode(cd) for cd in range(256)])
+    vd = dec[vc[:, :, :, :S]] * vs[:, :, :, None]
+    assert np.array_equal(vd, f64(v).transpose(0, 2, 3, 1))
+    rows = np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(S)])
+    got = oracle.sage_attn_rows(prep, S, rows)
+    ref = oracle.attn_rows(q, k, v, SCALE, rows=rows)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5 * np.abs(ref).max())
+
+
+def test_sage_attn_rows_single_key_and_equal_scores():
+    # S = 1: the output is the key's decoded V row.  Q = 0: every weight equal, so the output is
+    # the mean of the decoded V rows.
+    q, k, v = rand_qkv(1, 40, 2, seed=5)
+    for S in (1, 40):
+        qq = torch.zeros_like(q[:, :S]) if S > 1 else q[:, :S]
+        prep = oracle.sage_prepare(qq, k[:, :S], v[:, :S], SCALE)
+        qc, qs, kc, ks, vc, vs = prep
+        dec = np.array([oracle.e4m3_decode(cd) for cd in range(256)])
+        vd = dec[vc[:, :, :, :S]] * vs[:, :, :, None]          # [B, H, D, S]
+        rows = np.array([(0, h, i) for h in range(2) for i in range(S)])
+        got = oracle.sage_attn_rows(prep, S, rows)
+        want = np.stack([vd[0, r[1]].mean(axis=1) for r in rows])
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+
+
+def test_sage_attn_rows_error_is_the_quantizers():
+    # On randn inputs the quantized operands' attention stays within the gates the kernels are
+    # held to against exact attention (cosine >= 0.998, relative L2 <= 0.05), and is not exact
+    # (INT8 Q/K and FP8 V do change the result).
+    q, k, v = rand_qkv(1, 256, 2, seed=9)
+    rows = np.array([(0, h, i) for h in range(2) for i in range(0, 256, 3)])
+    got = oracle.sage_attn_rows(oracle.sage_prepare(q, k, v, SCALE), 256, rows)
+    ref = oracle.attn_rows(q, k, v, SCALE, rows=rows)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    cos = (got * ref).sum() / np.linalg.norm(got) / np.linalg.norm(ref)
+    assert 1e-3 < rel <= 0.05 and cos >= 0.998, (rel, cos)
