@@ -94,6 +94,9 @@ constexpr float kLazyThresh = 0.8f;
 // code step, which centres the error of the in-octave factor 1 + f against 2^f (0 to +0.69 steps).
 constexpr float kCodeSlope = 8.0f;
 constexpr float kCodeOffset = 56.0f - 0.35f;
+// Largest 8 s (code steps per int32 score unit times 2^26) for which the one-FMA code argument is
+// exact to about a fiftieth of a code step: kSeed * kFastS8 * 2^-24 = 0.02.
+constexpr float kFastS8 = 0x1p21f;
 // K Q^T accumulator seed: the bit pattern of 1/(2 pi) (0x3E22F983).  Its mantissa field, 2293123,
 // stays inside [0, 2^23) after adding any score (|score| <= 128 * 127^2 = 2064512): the int32
 // sum read as fp32 is exactly kSeed + score * 2^-26.
@@ -142,6 +145,7 @@ static_assert(NW * 64 == kSplitThreads && BQ == 256 && BK == 64,
 template <bool SK>
 __device__ __forceinline__ void sage_body(const SageArgs& a) {
   __shared__ __attribute__((aligned(16))) char lds[NSTAGE * (KT_BYTES + VT_BYTES) + NSTAGE * 16];  // 48 KB
+  __shared__ int large_w[NW];  // per wave: the large-scale code path is needed
 
   // One query tile L: the key tiles its window covers (tb < 0), or the tiles [tb, te) of a split
   // tail, ending by mode: kSplitFull writes O, kSplitPartial writes (acc, m, l) to the
@@ -388,7 +392,8 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
     // One body for every tile (two copies of it make the compiler double-allocate the
     // accumulators); a tile crossing a mask boundary only takes two small branches: its
     // hidden scores become INT32_MIN before the row max, and their P codes become 0.
-    auto softmax = [&](int t) __attribute__((always_inline)) {
+    auto softmax = [&](int t, auto large_c) __attribute__((always_inline)) {
+      constexpr bool kLarge = decltype(large_c)::value;
       if constexpr (!SK) row_max(t);
       const float s = s_tile;
       const bool masked = masked_tile(t);  // uniform
@@ -405,31 +410,44 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
       }
       // The code argument 8 x + kCodeOffset as ONE fma on the seeded pattern A = kSeed + score *
       // 2^-26, with s = q_scale * k_scale * 2^26 in base-2 units: A * 8 s + (mneg - kSeed * 8 s).
-      // The constant's rounding error is below a tenth of a code step.
+      // That constant is rounded at about kSeed * 8 s * 2^-24, a fiftieth of a code step while
+      // 8 s <= kFastS8 (every tile of inputs of ordinary magnitude).  For larger scales (|q| and |k|
+      // in the tens and beyond) a wave takes the score out of the pattern first, A - kSeed, which
+      // is exact (both share one exponent), and clamps the code argument at 126, so the codes stay
+      // right and never reach 127 (NaN) whatever the magnitude or the running max.
       const float s8 = kCodeSlope * s;
-      const float cst = fmaf(-kSeed, s8, mneg);
-      float y[32];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) y[16 * tt + r] = fmaf(__int_as_float(si[tt][r]), s8, cst);
-      if (masked) {
+      // P (B operand, 32 e4m3 bytes): byte e = key 32 hl + e.  v_cvt_pk_u8_f32 rounds to the
+      // nearest integer and clamps to [0, 255]; y <= 8 * 8.8 + 56 - 0.35 < 126.5 (and the large-scale
+      // path clamps at 126), so the largest code is 126 (448) and never 127 (NaN).  Every byte of
+      // the old word is overwritten.  Each path packs its own codes, so only P's eight registers
+      // meet after the branch.
+      auto codes = [&](auto large_c) __attribute__((always_inline)) {
+        constexpr bool large = decltype(large_c)::value;
+        const float cst = fmaf(-kSeed, s8, mneg);
+        float y[32];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) y[16 * tt + r] = si[tt][r] == kMasked ? -1.0f : y[16 * tt + r];
-      }
-      // P (B operand, 32 e4m3 bytes): byte e = key 32 hl + e.  v_cvt_pk_u8_f32 rounds to the
-      // nearest integer and clamps to [0, 255]; y <= 8 * 8.8 + 56 - 0.35 < 126.5, so the largest
-      // code is 126 (448) and never 127 (NaN).  Every byte of the old word is overwritten.
+          for (int r = 0; r < 16; ++r) {
+            const float A = __int_as_float(si[tt][r]);
+            y[16 * tt + r] = large ? fminf(fmaf(A - kSeed, s8, mneg), 126.0f) : fmaf(A, s8, cst);
+          }
+        if (masked) {
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        uint32_t word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w], 0, (uint32_t)pf[w]);
-        word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 1], 1, word);
-        word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 2], 2, word);
-        word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 3], 3, word);
-        pf[w] = (int)word;
-      }
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) y[16 * tt + r] = si[tt][r] == kMasked ? -1.0f : y[16 * tt + r];
+        }
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          uint32_t word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w], 0, (uint32_t)pf[w]);
+          word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 1], 1, word);
+          word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 2], 2, word);
+          word = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * w + 3], 3, word);
+          pf[w] = (int)word;
+        }
+      };
+      codes(std::integral_constant<bool, kLarge>{});
       // keep the softmax in its phase: without the pin the compiler sinks the
       // code conversions past the barrier, next to the P V products that consume them
       asm volatile("" : "+v"(pf));
@@ -477,15 +495,15 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
     // phase before that barrier (one full window after the issue).  The stages they refill
     // held K(q-1) and V(q-2), last read in M(q-1), finished by both groups at barrier 2q.
     // The k_scale pair of a tile is read in the M phase with its K rows.
-    auto period = [&](auto st_c, int p) __attribute__((always_inline)) {  // 1 <= p <= n - 1, st = p % 3
-      constexpr int st = decltype(st_c)::value;
+    auto period = [&](auto st_c, int p, auto large_c) __attribute__((always_inline)) {  // 1 <= p <= n - 1
+      constexpr int st = decltype(st_c)::value;  // p % 3
       using KS = std::integral_constant<int, st>;
       using VS = std::integral_constant<int, (st + NSTAGE - 1) % NSTAGE>;
       copy(p);
       mphase(VS{}, KS{}, T{}, T{}, t0 + p);
       if (!grp_a) prev_landed(p);
       barrier();
-      softmax(t0 + p);
+      softmax(t0 + p, large_c);
       if (grp_a) prev_landed(p);
       barrier();
     };
@@ -493,35 +511,60 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
     issue_k(t0, 0);
     if (n > 1) issue_k(t0 + 1, 1);
     issue_v(t0, 0);
+    // The code path of the softmax (below) is chosen once per workgroup and query tile (or piece
+    // of one), from the largest k_scale of the key blocks it visits, loaded under the first
+    // copies: the large-scale path only where a wave's 8 s could exceed kFastS8 on some tile.
+    // Choosing it per tile instead cost 2 to 4 %: its code in the loop changed how the compiler
+    // laid out the fast one.
+    {
+      float kmax = 0.0f;
+      const int b0 = 2 * t0, b1 = min(2 * t1, nblk_k);
+#pragma unroll 4
+      for (int i = b0 + tid; i < b1; i += NW * 64) kmax = fmaxf(kmax, ksc[i]);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off, 64));
+      if (l == 0) large_w[wave] = kCodeSlope * sq * kmax > kFastS8 ? 1 : 0;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the flag is in LDS before the barrier
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier();  // barrier 0
     if (!grp_a) barrier();  // group B's leading barrier (barrier 1 for group A)
-    // period 0: no P V yet, no window before it to wait for
-    copy(0);
-    mphase(I0{}, I0{}, F{}, T{}, t0);
-    barrier();
-    softmax(t0);
-    barrier();
-    int p = 1;
-    for (; p + 2 < n; p += 3) {  // three periods per trip: stage offsets are immediates
-      period(I1{}, p);
-      period(I2{}, p + 1);
-      period(I0{}, p + 2);
+    bool large = false;
+    {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) large = large || large_w[w] != 0;
     }
-    if (p < n) {
-      period(I1{}, p);
-      ++p;
-    }
-    if (p < n) {
-      period(I2{}, p);
-      ++p;
-    }
-    // M(n): P V of the last tile (n - 1) from V stage (n - 1) % 3
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const int vs_last = (n - 1) % NSTAGE;
-    if (vs_last == 0) mphase(I0{}, I0{}, T{}, F{}, 0);
-    else if (vs_last == 1) mphase(I1{}, I0{}, T{}, F{}, 0);
-    else mphase(I2{}, I0{}, T{}, F{}, 0);
+    auto key_loop = [&](auto large_c) __attribute__((always_inline)) {
+      // period 0: no P V yet, no window before it to wait for
+      copy(0);
+      mphase(I0{}, I0{}, F{}, T{}, t0);
+      barrier();
+      softmax(t0, large_c);
+      barrier();
+      int p = 1;
+      for (; p + 2 < n; p += 3) {  // three periods per trip: stage offsets are immediates
+        period(I1{}, p, large_c);
+        period(I2{}, p + 1, large_c);
+        period(I0{}, p + 2, large_c);
+      }
+      if (p < n) {
+        period(I1{}, p, large_c);
+        ++p;
+      }
+      if (p < n) {
+        period(I2{}, p, large_c);
+        ++p;
+      }
+      // M(n): P V of the last tile (n - 1) from V stage (n - 1) % 3
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const int vs_last = (n - 1) % NSTAGE;
+      if (vs_last == 0) mphase(I0{}, I0{}, T{}, F{}, 0);
+      else if (vs_last == 1) mphase(I1{}, I0{}, T{}, F{}, 0);
+      else mphase(I2{}, I0{}, T{}, F{}, 0);
+    };
+    if (large) key_loop(std::true_type{});
+    else key_loop(std::false_type{});
     if (grp_a) barrier();  // matches group B's leading barrier
   }
 
@@ -542,13 +585,17 @@ __device__ __forceinline__ void sage_body(const SageArgs& a) {
   // (NaN if a piece never came)
   const float inv = !ok ? __builtin_nanf("") : (lsum > 0.0f ? 1.0f / lsum : 0.0f);
   if (qi < a.S_q) {
+    // the lane's channel offset, opaque here: hoisted out of the split kernel's loop over work
+    // items, its 64-bit output address stayed live across the key loop and spilled
+    int hl_e = hl;
+    asm volatile("" : "+v"(hl_e));
     const float* vsc = a.v_scale + (int64_t)bhk * kHeadDim;
     __bf16* orow = (__bf16*)a.o + (((int64_t)b * a.S_q + qi) * a.H + h) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d = 32 * dt + 8 * rq + 4 * hl;
+        const int d = 32 * dt + 8 * rq + 4 * hl_e;
         const f32x4 s4 = *(const f32x4*)(vsc + d);
         bf16x4 ov;
 #pragma unroll
