@@ -10,6 +10,10 @@ Gates (from the DiT attention workloads' acceptance criteria):
     at most 0.5 % of elements outside the band |got - ref| <= 0.3 + 0.25 |ref|
     (the band of the quantized op's test plan on the aiter PR page,
     "gfx1201_sage_prepare / gfx1201_sage_attention", section "Test Plan").
+    The same cosine and relative-L2 gates hold on 512 of the rows against
+    attention of the quantized operands (the oracle's quantizer, then exact
+    fp64 attention on its codes and scales): the kernel's own error, without
+    the quantizer's.
 Set DITATTN_PARITY_LOG=<file> to append one JSON line of metrics per check.
 Small shapes check every output row; the DiT-sized workloads check a seeded
 sample of 4096 query rows that always includes the last 32 rows of the first
@@ -144,6 +148,13 @@ def test_sage_attention_matches_oracle(case):
     assert mt["rel_l2"] <= SAGE_MAX_REL_L2, mt
     assert mt["median_row_cos"] >= SAGE_MIN_MEDIAN_ROW_COS, mt
     assert mt["band_frac"] <= BAND_MAX_FRAC, mt
+    n = min(512, len(case.rows))
+    log("[sage %s] oracle: attention of the quantized operands on %d rows" % (w.name, n))
+    ref_q = oracle.sage_attn_rows(case.prep_ref, w.S, case.rows[:n])
+    mq = metrics(got[:n], ref_q)
+    log("[sage %s] vs quantized operands: %s" % (w.name, mq))
+    record("sage_vs_quantized", w.name, mq)
+    assert mq["cos"] >= SAGE_MIN_COS and mq["rel_l2"] <= SAGE_MAX_REL_L2, mq
 
 
 # ---------------------------------------------------------------- edge shapes
