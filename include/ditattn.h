@@ -282,6 +282,10 @@ int qk_norm_rope_bf16(const void* x, void* out, int B, int S, int H, int D, cons
  * Scores s = int32(q_code . k_code) * q_scale * k_scale are in base-2 units.
  * Keys j >= S are masked.  P is rounded to FP8 e4m3 as p * 2^8 and the row sum
  * l is taken over the same FP8 values; o = acc * v_scale / l.
+ * Any magnitude: a workgroup whose q_scale * k_scale exceeds 2^-8 on some tile
+ * (|q| and |k| in the tens and beyond) makes P's codes from the exact score
+ * rather than the one-FMA form, whose rounding would grow with the scales; the
+ * output stays finite while 2^29 * q_scale * k_scale is a finite fp32 value.
  */
 int sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                   const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* o,
