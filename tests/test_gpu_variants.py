@@ -5,7 +5,8 @@ masking, one- and two-sided sliding windows).
 
 Gates as for self-attention (BF16: max abs <= 1e-2, cosine >= 0.99999; Sage:
 cosine >= 0.998, relative L2 <= 5e-2), over the rows that see at least one key;
-a row that sees none must be exactly zero.
+a row that sees none must be exactly zero.  Besides the listed cases, 40 seeded
+random shapes and windows cover the same classes.
 """
 import json
 import math
@@ -129,3 +130,49 @@ def test_windowed_variants_deterministic():
         sb = ia.sage_attention_ex(q, k, v, SCALE, window)
         torch.cuda.synchronize()
         assert torch.equal(a, b) and torch.equal(sa, sb)
+
+
+def random_cases(n=40, seed=2024):
+    """n seeded shapes across the variants: B <= 2, 64 <= S_q, S_kv <= 1600 (lengths on and off
+    the 32-row and 64-key tile edges), H_kv dividing H, and a window that is none, causal, or
+    one- or two-sided with widths from 0 to past the sequence."""
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(g.integers(1, 3))
+        S_q = int(g.choice([g.integers(64, 1601), 64 * g.integers(1, 26), 32 * g.integers(2, 51) + 1]))
+        S_kv = int(g.choice([S_q, g.integers(64, 1601), 64 * g.integers(1, 26) - 1]))
+        H_kv = int(g.integers(1, 4))
+        H = H_kv * int(g.choice([1, 2, 4]))
+        kind = g.integers(0, 4)
+        if kind == 0:
+            w = (-1, -1)
+        elif kind == 1:
+            w = (-1, 0)
+        elif kind == 2:
+            w = (int(g.integers(0, 2 * S_kv)), 0)
+        else:
+            w = (int(g.integers(0, S_kv)), int(g.integers(0, S_kv)))
+        out.append((B, S_q, S_kv, H, H_kv, w))
+    return out
+
+
+RANDOM = random_cases()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("c", RANDOM, ids=[case_id(c) for c in RANDOM])
+def test_random_shapes_both_modes(c):
+    B, S_q, S_kv, H, H_kv, window = c
+    name = case_id(c)
+    log("[random %s]" % name)
+    q, k, v = inputs(B, S_q, S_kv, H, H_kv, seed=7 * S_q + S_kv + 11 * H, k_bias_std=2.0)
+    rows = synth.sample_rows(B, S_q, H, n=1024, seed=S_q * 3 + S_kv)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = ia.attn_fwd_bf16_ex(qd, kd, vd, SCALE, window)
+    sout = ia.sage_attention_ex(qd, kd, vd, SCALE, window)
+    torch.cuda.synchronize()
+    mt = check("bf16 " + name, out, q, k, v, window, rows)
+    assert mt["max_abs"] <= 1e-2 and mt["cos"] >= 0.99999, mt
+    ms = check("sage " + name, sout, q, k, v, window, rows)
+    assert ms["cos"] >= 0.998 and ms["rel_l2"] <= 5e-2, ms
