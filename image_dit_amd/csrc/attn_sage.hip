@@ -33,7 +33,10 @@
 //     byte (clamped at 0: p * 2^8 below 2^-7 becomes 0).  Two vector
 //     instructions per score instead of FMA, exp2 and half an FP8 packing;
 //     the relative L2 error of O against exact attention rises from about
-//     0.042 to 0.045 (gate 0.05).
+//     0.042 to 0.045 (gate 0.05).  That FMA cancels a constant that grows with
+//     the scales; a workgroup whose q_scale * k_scale exceeds 2^-8 on some tile
+//     (|q|, |k| in the tens and beyond) takes the score out of the pattern
+//     first and clamps the argument at 126 (code 127 is NaN).
 //   * Matrix phase reads are issued as explicit LDS instructions ahead of the
 //     MFMAs that take them: four K fragments, the tile's k_scale pair and two
 //     V^T fragments at the start of the phase, then one K fragment (later two
