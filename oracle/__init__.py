@@ -70,10 +70,12 @@ def _lib():
         lib.oracle_qk_norm_rope.argtypes = [u16p, ci, ci, ci, ci, u16p, cf, u16p, u16p, ci, u16p]
         lib.oracle_sage_attn_rows.argtypes = [i8p, f32p, i8p, f32p, u8p, f32p, ci, ci, ci, ci, ci,
                                               i64p, ctypes.c_int64, f64p, ci]
+        lib.oracle_sage_attn_rows_ex.argtypes = [i8p, f32p, i8p, f32p, u8p, f32p, ci, ci, ci, ci, ci,
+                                                 ci, ci, ci, ci, ci, i64p, ctypes.c_int64, f64p, ci]
         for name in ("oracle_softmax_row", "oracle_attn_rows", "oracle_attn_blocked",
                      "oracle_quant_qk", "oracle_quant_v", "oracle_qk_norm_rope",
                      "oracle_quant_qk_mean", "oracle_channel_mean", "oracle_attn_rows_ex",
-                     "oracle_sage_attn_rows"):
+                     "oracle_sage_attn_rows", "oracle_sage_attn_rows_ex"):
             getattr(lib, name).restype = ci
         _LIB = lib
     return _LIB
@@ -265,6 +267,31 @@ def sage_attn_rows(prepared, S, rows, nthreads=0):
                                         B, S, H, D, S_pad, _ptr(rows, ctypes.c_int64),
                                         rows.shape[0], _ptr(out, ctypes.c_double), nthreads),
            "oracle_sage_attn_rows")
+    return out
+
+
+def sage_attn_rows_ex(prepared, S_q, S_kv, window=(-1, -1), rows=None, nthreads=0):
+    """sage_attn_rows for the prepared tensors of sage_prepare_ex: Q codes [B, H, S_q_pad, D],
+    K/V of H_kv heads and S_kv real tokens (query head h reads head h // (H // H_kv)), and the
+    key window of attn_rows_ex; a row that sees no key is 0.  Returns [n, D]."""
+    qc, qs, kc, ks, vc, vs = (np.ascontiguousarray(a) for a in prepared[:6])
+    B, H, S_q_pad, D = qc.shape
+    _, H_kv, S_kv_pad, _ = kc.shape
+    assert qc.dtype == np.int8 and kc.dtype == np.int8 and vc.dtype == np.uint8
+    assert qs.dtype == np.float32 and ks.dtype == np.float32 and vs.dtype == np.float32
+    assert vc.shape == (B, H_kv, D, S_kv_pad) and vs.shape == (B, H_kv, D)
+    assert qs.shape == (B, H, S_q_pad // 32) and ks.shape == (B, H_kv, S_kv_pad // 32)
+    assert 0 < S_q <= S_q_pad and 0 < S_kv <= S_kv_pad
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], D), dtype=np.float64)
+    _check(_lib().oracle_sage_attn_rows_ex(_ptr(qc, ctypes.c_int8), _ptr(qs, ctypes.c_float),
+                                           _ptr(kc, ctypes.c_int8), _ptr(ks, ctypes.c_float),
+                                           _ptr(vc, ctypes.c_uint8), _ptr(vs, ctypes.c_float),
+                                           B, S_q, S_kv, H, H_kv, D, S_q_pad, S_kv_pad,
+                                           int(window[0]), int(window[1]),
+                                           _ptr(rows, ctypes.c_int64), rows.shape[0],
+                                           _ptr(out, ctypes.c_double), nthreads),
+           "oracle_sage_attn_rows_ex")
     return out
 
 

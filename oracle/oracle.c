@@ -585,24 +585,29 @@ int oracle_attn_rows_ex(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 /* ------------------------------------------------------------------------ */
 /* 4. Attention of the quantized operands                                     */
 /* ------------------------------------------------------------------------ */
-
 /*
  * For each row (b, h, i) of rows (nrows triples), with the codes and scales in
- * the layouts oracle_quant_qk and oracle_quant_v write (S real tokens of S_pad):
- *   x_j = (sum_d qc[b,h,i,d] * kc[b,h,j,d]) * qs[b,h,i/32] * ks[b,h,j/32],  j < S
- *   p_j = 2^(x_j - max_j x_j)
- *   out[r][d] = vs[b,h,d] * (sum_j p_j * e4m3(vc[b,h,d,j])) / (sum_j p_j)
- * The dot products of codes are exact integers; the rest is fp64.
+ * the layouts oracle_quant_qk and oracle_quant_v write: Q [B, H, S_q_pad, D],
+ * K [B, H_kv, S_kv_pad, D], V [B, H_kv, D, S_kv_pad]; query head h reads key /
+ * value head h / (H / H_kv), and sees key j when lo(i) <= j <= hi(i) with the
+ * window of oracle_attn_rows_ex (lo = i + S_kv - S_q - wl, hi = i + S_kv - S_q + wr,
+ * a negative bound meaning none on that side):
+ *   x_j = (sum_d qc[b,h,i,d] * kc[b,hk,j,d]) * qs[b,h,i/32] * ks[b,hk,j/32]
+ *   p_j = 2^(x_j - max x)   over the keys the query sees
+ *   out[r][d] = vs[b,hk,d] * (sum_j p_j * e4m3(vc[b,hk,d,j])) / (sum_j p_j),
+ * or 0 for a row that sees no key.  The dot products of codes are exact
+ * integers; the rest is fp64.
  */
-int oracle_sage_attn_rows(const int8_t* qc, const float* qs, const int8_t* kc, const float* ks,
-                          const uint8_t* vc, const float* vs, int B, int S, int H, int D,
-                          int S_pad, const int64_t* rows, int64_t nrows, double* out,
-                          int nthreads) {
-  if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || S_pad < S || S_pad % 32 != 0 || nrows < 0)
+int oracle_sage_attn_rows_ex(const int8_t* qc, const float* qs, const int8_t* kc, const float* ks,
+                             const uint8_t* vc, const float* vs, int B, int S_q, int S_kv, int H,
+                             int H_kv, int D, int S_q_pad, int S_kv_pad, int wl, int wr,
+                             const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (B <= 0 || S_q <= 0 || S_kv <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || D <= 0 ||
+      S_q_pad < S_q || S_kv_pad < S_kv || S_q_pad % 32 != 0 || S_kv_pad % 32 != 0 || nrows < 0)
     return ORACLE_EINVAL;
   for (int64_t r = 0; r < nrows; ++r) {
     if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= H ||
-        rows[3 * r + 2] < 0 || rows[3 * r + 2] >= S)
+        rows[3 * r + 2] < 0 || rows[3 * r + 2] >= S_q)
       return ORACLE_EINVAL;
   }
 #ifdef _OPENMP
@@ -610,10 +615,11 @@ int oracle_sage_attn_rows(const int8_t* qc, const float* qs, const int8_t* kc, c
 #else
   (void)nthreads;
 #endif
+  const int group = H / H_kv;
   int status = ORACLE_OK;
 #pragma omp parallel num_threads(nt)
   {
-    double* x = (double*)malloc(sizeof(double) * (size_t)S);
+    double* x = (double*)malloc(sizeof(double) * (size_t)S_kv);
     if (!x) {
 #pragma omp atomic write
       status = ORACLE_ENOMEM;
@@ -622,30 +628,46 @@ int oracle_sage_attn_rows(const int8_t* qc, const float* qs, const int8_t* kc, c
     for (int64_t r = 0; r < nrows; ++r) {
       if (!x) continue;
       const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
-      const int64_t bh = b * H + h;
-      const int8_t* qrow = qc + (bh * S_pad + i) * D;
-      const double q_s = (double)qs[bh * (S_pad / 32) + i / 32];
+      const int64_t bh = b * H + h, bk = b * H_kv + h / group;
+      const int64_t c = i + S_kv - S_q;
+      const int64_t lo = wl >= 0 ? (c - wl > 0 ? c - wl : 0) : 0;
+      const int64_t hi = wr >= 0 ? (c + wr < S_kv - 1 ? c + wr : S_kv - 1) : S_kv - 1;
+      if (lo > hi) {
+        for (int d = 0; d < D; ++d) out[r * D + d] = 0.0;
+        continue;
+      }
+      const int8_t* qrow = qc + (bh * S_q_pad + i) * D;
+      const double q_s = (double)qs[bh * (S_q_pad / 32) + i / 32];
       double xmax = -INFINITY;
-      for (int j = 0; j < S; ++j) {
-        const int8_t* krow = kc + (bh * S_pad + j) * D;
+      for (int64_t j = lo; j <= hi; ++j) {
+        const int8_t* krow = kc + (bk * S_kv_pad + j) * D;
         int64_t dot = 0;
         for (int d = 0; d < D; ++d) dot += (int64_t)qrow[d] * (int64_t)krow[d];
-        x[j] = (double)dot * q_s * (double)ks[bh * (S_pad / 32) + j / 32];
+        x[j] = (double)dot * q_s * (double)ks[bk * (S_kv_pad / 32) + j / 32];
         if (x[j] > xmax) xmax = x[j];
       }
       double l = 0.0;
-      for (int j = 0; j < S; ++j) {
+      for (int64_t j = lo; j <= hi; ++j) {
         x[j] = exp2(x[j] - xmax);
         l += x[j];
       }
       for (int d = 0; d < D; ++d) {
-        const uint8_t* vrow = vc + (bh * D + d) * S_pad;
+        const uint8_t* vrow = vc + (bk * D + d) * S_kv_pad;
         double acc = 0.0;
-        for (int j = 0; j < S; ++j) acc += x[j] * oracle_e4m3_decode(vrow[j]);
-        out[r * D + d] = (double)vs[bh * D + d] * acc / l;
+        for (int64_t j = lo; j <= hi; ++j) acc += x[j] * oracle_e4m3_decode(vrow[j]);
+        out[r * D + d] = (double)vs[bk * D + d] * acc / l;
       }
     }
     free(x);
   }
   return status;
+}
+
+/* Self-attention without a window: oracle_sage_attn_rows_ex with S_q = S_kv = S, H_kv = H. */
+int oracle_sage_attn_rows(const int8_t* qc, const float* qs, const int8_t* kc, const float* ks,
+                          const uint8_t* vc, const float* vs, int B, int S, int H, int D,
+                          int S_pad, const int64_t* rows, int64_t nrows, double* out,
+                          int nthreads) {
+  return oracle_sage_attn_rows_ex(qc, qs, kc, ks, vc, vs, B, S, S, H, H, D, S_pad, S_pad, -1, -1,
+                                  rows, nrows, out, nthreads);
 }

@@ -5,8 +5,10 @@ masking, one- and two-sided sliding windows).
 
 Gates as for self-attention (BF16: max abs <= 1e-2, cosine >= 0.99999; Sage:
 cosine >= 0.998, relative L2 <= 5e-2), over the rows that see at least one key;
-a row that sees none must be exactly zero.  Besides the listed cases, 40 seeded
-random shapes and windows cover the same classes.
+a row that sees none must be exactly zero.  The Sage output meets the same
+cosine and relative-L2 gates against attention of the oracle's quantized
+operands (its own error, without the quantizer's).  Besides the listed cases, 40
+seeded random shapes and windows cover the same classes.
 """
 import json
 import math
@@ -53,11 +55,15 @@ def seen_rows(S_q, S_kv, wl, wr):
     return lo <= hi
 
 
-def check(name, got_gpu, q, k, v, window, rows):
-    """Compare the sampled rows (b, h, i) of got_gpu [B, S_q, H, 128] with the oracle."""
+def check(name, got_gpu, q, k, v, window, rows, quantized=False):
+    """Compare the sampled rows (b, h, i) of got_gpu [B, S_q, H, 128] with the oracle's exact
+    attention, or with quantized=True with attention of the oracle's quantized operands."""
     B, S_q, H, _ = q.shape
     S_kv = k.shape[1]
-    ref = oracle.attn_rows_ex(q, k, v, SCALE, window, rows=rows)
+    if quantized:
+        ref = oracle.sage_attn_rows_ex(oracle.sage_prepare_ex(q, k, v, SCALE), S_q, S_kv, window, rows)
+    else:
+        ref = oracle.attn_rows_ex(q, k, v, SCALE, window, rows=rows)
     idx = torch.from_numpy(rows).to(got_gpu.device)
     got = got_gpu[idx[:, 0], idx[:, 2], idx[:, 1]].float().cpu().numpy().astype(np.float64)
     seen = seen_rows(S_q, S_kv, *window)[rows[:, 2]]
@@ -112,6 +118,9 @@ def test_variant_both_modes(c):
     ms = check("sage " + name, sout, q, k, v, window, rows)
     record("sage_variant", name, ms)
     assert ms["cos"] >= 0.998 and ms["rel_l2"] <= 5e-2, ms
+    mq = check("sage vs quantized operands " + name, sout, q, k, v, window, rows, quantized=True)
+    record("sage_variant_vs_quantized", name, mq)
+    assert mq["cos"] >= 0.998 and mq["rel_l2"] <= 5e-2, mq
 
 
 def test_ex_entry_points_equal_the_plain_ones():
@@ -176,3 +185,5 @@ def test_random_shapes_both_modes(c):
     assert mt["max_abs"] <= 1e-2 and mt["cos"] >= 0.99999, mt
     ms = check("sage " + name, sout, q, k, v, window, rows)
     assert ms["cos"] >= 0.998 and ms["rel_l2"] <= 5e-2, ms
+    mq = check("sage vs quantized operands " + name, sout, q, k, v, window, rows, quantized=True)
+    assert mq["cos"] >= 0.998 and mq["rel_l2"] <= 5e-2, mq

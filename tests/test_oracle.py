@@ -586,23 +586,23 @@ def test_thread_count_of_one_call_does_not_stick():
 # attention of the quantized operands
 # --------------------------------------------------------------------------
 
-def exactly_quantizable(B, S, H, seed, D=128):
-    """BF16 Q, K, V that the quantizer represents exactly: each 32-row Q/K block holds integers
-    c in [-127, 127] (one of them +-127) times its own power of two, and each V channel holds
-    E4M3 values (one of them +-448) times its own power of two."""
-    g = np.random.default_rng(seed)
+def exact_qk(g, B, S, H, D=128):
+    """Q or K values the quantizer represents exactly: each 32-row block holds integers c in
+    [-127, 127] (one of them +-127) times its own power of two."""
     nblk = -(-S // 32)
+    c = g.integers(-127, 128, size=(B, S, H, D))
+    e = g.integers(-7, -4, size=(B, nblk, H))          # 2^-7 .. 2^-5 per block
+    for b in range(B):
+        for blk in range(nblk):
+            for h in range(H):
+                c[b, 32 * blk + g.integers(0, min(32, S - 32 * blk)), h, g.integers(0, D)] = \
+                    127 * (1 if g.random() < 0.5 else -1)
+    return bf16(c * np.exp2(np.repeat(e, 32, axis=1)[:, :S, :, None]))
 
-    def qk():
-        c = g.integers(-127, 128, size=(B, S, H, D))
-        e = g.integers(-7, -4, size=(B, nblk, H))          # 2^-7 .. 2^-5 per block
-        for b in range(B):
-            for blk in range(nblk):
-                for h in range(H):
-                    c[b, 32 * blk + g.integers(0, min(32, S - 32 * blk)), h, g.integers(0, D)] = \
-                        127 * (1 if g.random() < 0.5 else -1)
-        return c * np.exp2(np.repeat(e, 32, axis=1)[:, :S, :, None])
 
+def exact_v(g, B, S, H, D=128):
+    """V values the quantizer represents exactly: each channel holds E4M3 values (one of them
+    448) times its own power of two."""
     mags = np.array([oracle.e4m3_decode(cd) for cd in range(127)])
     vm = mags[g.integers(0, 127, size=(B, S, H, D))] * np.where(g.random((B, S, H, D)) < 0.5, 1, -1)
     for b in range(B):
@@ -610,8 +610,12 @@ def exactly_quantizable(B, S, H, seed, D=128):
             for d in range(D):
                 vm[b, g.integers(0, S), h, d] = 448.0
     ev = g.integers(-10, -5, size=(B, 1, H, D))             # 2^-10 .. 2^-6 per channel
-    v = vm * np.exp2(ev)
-    return tuple(bf16(x) for x in (qk(), qk(), v))
+    return bf16(vm * np.exp2(ev))
+
+
+def exactly_quantizable(B, S, H, seed, D=128):
+    g = np.random.default_rng(seed)
+    return exact_qk(g, B, S, H, D), exact_qk(g, B, S, H, D), exact_v(g, B, S, H, D)
 
 
 @pytest.mark.parametrize("B,S,H", [(1, 64, 1), (2, 100, 3)])
@@ -664,3 +668,23 @@ def test_sage_attn_rows_error_is_the_quantizers():
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     cos = (got * ref).sum() / np.linalg.norm(got) / np.linalg.norm(ref)
     assert 1e-3 < rel <= 0.05 and cos >= 0.998, (rel, cos)
+
+
+@pytest.mark.parametrize("B,S_q,S_kv,H,H_kv,window", [
+    (2, 70, 300, 4, 2, (-1, -1)),    # cross-attention, grouped heads, S_kv padded to 512
+    (1, 150, 70, 3, 1, (-1, 0)),     # causal with S_q > S_kv: the first 80 rows see no key
+    (1, 100, 100, 2, 2, (20, 5)),    # two-sided window
+    (1, 1, 90, 4, 4, (-1, 0)),       # a decode step sees every key
+])
+def test_sage_attn_rows_ex_is_exact_windowed_attention_on_exact_codes(B, S_q, S_kv, H, H_kv, window):
+    # as above, with the key/value head of each query head, the window and empty rows
+    g = np.random.default_rng(S_q * 7 + S_kv)
+    q, k, v = exact_qk(g, B, S_q, H), exact_qk(g, B, S_kv, H_kv), exact_v(g, B, S_kv, H_kv)
+    prep = oracle.sage_prepare_ex(q, k, v, SCALE)
+    rows = np.array([(b, h, i) for b in range(B) for h in range(H) for i in range(S_q)])
+    got = oracle.sage_attn_rows_ex(prep, S_q, S_kv, window, rows)
+    ref = oracle.attn_rows_ex(q, k, v, SCALE, window, rows=rows)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-5 * np.abs(ref).max())
+    if window == (-1, 0) and S_q > S_kv:
+        assert not got[rows[:, 2] < S_q - S_kv].any()
+
