@@ -8,7 +8,8 @@ the same running-max rescaling the blocked form uses; the quantized operands are
     the BF16 path, and not for shapes with fewer than three whole rounds of query tiles;
   * against exact fp64 attention on the BF16 inputs: the Sage gates (cosine >= 0.998,
     relative L2 <= 5e-2), with an error no larger than sage_attn_fwd_ex's (P is rounded to FP8
-    relative to each piece's own running max, so the two outputs differ by that rounding);
+    relative to each piece's own running max, so the two outputs differ by that rounding); the
+    same gates against attention of the oracle's quantized operands;
   * run-to-run bitwise deterministic, also when one workspace serves consecutive calls;
   * shapes that are not split give exactly sage_attn_fwd_ex's output.
 """
@@ -76,6 +77,13 @@ def test_sage_split_matches_oracle_and_unsplit(shape):
         log("  %s: cos %.5f relL2 %.4f max abs %.2e" % (name, cos, rel[name], float(np.max(np.abs(got - ref)))))
         assert cos >= 0.998 and rel[name] <= 5e-2, (name, cos, rel[name])
     assert rel["split"] <= 1.05 * rel["unsplit"] + 1e-3, rel
+    # the kernel's own error: against attention of the oracle's quantized operands
+    ref_q = oracle.sage_attn_rows_ex(oracle.sage_prepare_ex(qc, kc, vc, SCALE), S_q, S_kv, (-1, -1), rows)
+    got = o1[idx[:, 0], idx[:, 2], idx[:, 1]].float().cpu().numpy().astype(np.float64)
+    cos = float((got * ref_q).sum() / np.linalg.norm(got) / np.linalg.norm(ref_q))
+    rel_q = float(np.linalg.norm(got - ref_q) / np.linalg.norm(ref_q))
+    log("  split vs quantized operands: cos %.5f relL2 %.4f" % (cos, rel_q))
+    assert cos >= 0.998 and rel_q <= 5e-2, (cos, rel_q)
 
 
 @pytest.mark.parametrize("shape", [(1, 4096, 4096, 16, 16), (1, 300, 300, 2, 2), (1, 2000, 2000, 64, 8),
