@@ -133,6 +133,17 @@ def _on_stream(tensors, stream):
         t.record_stream(stream)
 
 
+def _zeroed_workspace(nbytes, device, stream):
+    """A zero-filled byte buffer for a split-tail call on `stream`: the fill runs on the
+    current stream, so `stream` (when it is another one) waits for it before the kernel."""
+    import torch
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        stream.wait_stream(torch.cuda.current_stream(device))
+        buf.record_stream(stream)
+    return buf
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
@@ -269,8 +280,7 @@ def attn_fwd_bf16_ws(q, k, v, scale, window=(-1, -1), out=None, workspace=None, 
     ws_bytes = 0
     if need:
         if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
-            _on_stream([workspace], stream)
+            workspace = _zeroed_workspace(need, q.device, stream)
         ws_bytes = _check_workspace(workspace, need, q.device)
     with _on_device(q.device):
         st = lib.attn_fwd_bf16_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S_q, S_kv, H, H_kv, D,
@@ -532,8 +542,7 @@ def sage_attn_fwd_ws(prepared, S_q, S_kv, H, H_kv, scale, window=(-1, -1), out=N
     ws_bytes = 0
     if need:
         if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
-            _on_stream([workspace], stream)
+            workspace = _zeroed_workspace(need, dev, stream)
         ws_bytes = _check_workspace(workspace, need, dev)
     with _on_device(dev):
         st = lib.sage_attn_fwd_ws(*[_ptr(t) for t in prepared], _ptr(out), B, int(S_q), int(S_kv), int(H),

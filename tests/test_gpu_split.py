@@ -96,3 +96,25 @@ def test_unsplit_shapes_equal_ex(shape):
 def test_windowed_calls_are_not_split():
     assert ia.bf16_workspace_size(1, 4608, 4608, 24, 24, (-1, 0)) == 0
     assert ia.bf16_workspace_size(1, 4608, 4608, 24, 24, (256, 256)) == 0
+
+
+def test_split_on_another_stream_equals_the_current_stream():
+    # Both split-tail entry points on a second stream with the binding's own workspace: its
+    # zero fill runs on the current stream and the second stream waits for it, so every call
+    # gives the output of the current-stream call bit for bit.
+    B, S, H = 1, 4608, 48
+    log("[split on another stream B=%d S=%d H=%d]" % (B, S, H))
+    assert ia.bf16_workspace_size(B, S, S, H, H) > 0
+    g = torch.Generator().manual_seed(95)
+    q, k, v = (torch.randn(B, S, H, 128, generator=g).to(torch.bfloat16).cuda() for _ in range(3))
+    prepared = ia.sage_prepare_ex(q, k, v, SCALE)
+    ref_b = ia.attn_fwd_bf16_ws(q, k, v, SCALE)
+    ref_s = ia.sage_attn_fwd_ws(prepared, S, S, H, H, SCALE)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = [(ia.attn_fwd_bf16_ws(q, k, v, SCALE, stream=side),
+             ia.sage_attn_fwd_ws(prepared, S, S, H, H, SCALE, stream=side)) for _ in range(3)]
+    torch.cuda.synchronize()
+    for ob, os_ in outs:
+        assert torch.equal(ob.view(torch.int16), ref_b.view(torch.int16))
+        assert torch.equal(os_.view(torch.int16), ref_s.view(torch.int16))
