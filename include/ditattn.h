@@ -228,7 +228,8 @@ int sage_prepare_ex_noalloc(const void* q, const void* k, const void* v, int8_t*
  * checks and status codes as attn_fwd_bf16_ex, plus:
  *   workspace        device pointer, 16-byte aligned, overlapping no tensor, at least
  *                    ditattn_bf16_workspace_size(...) bytes (owned by the caller and
- *                    zero-filled before its first use; later calls need no clearing);
+ *                    zero-filled before its first use, the fill complete or ordered
+ *                    before the call on its stream; later calls need no clearing);
  *                    may be NULL when that size is 0
  *   workspace_bytes  its size; too small -> DITATTN_EINVAL before anything is enqueued
  * When the size is 0 (key window on, fewer than three whole rounds of query tiles, one
@@ -311,7 +312,8 @@ int sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i
  * arguments, checks and status codes as sage_attn_fwd_ex, plus:
  *   workspace        device pointer, 16-byte aligned, overlapping no tensor, at least
  *                    ditattn_sage_attn_workspace_size(...) bytes (owned by the caller and
- *                    zero-filled before its first use; later calls need no clearing);
+ *                    zero-filled before its first use, the fill complete or ordered
+ *                    before the call on its stream; later calls need no clearing);
  *                    may be NULL when that size is 0
  *   workspace_bytes  its size; too small -> DITATTN_EINVAL before anything is enqueued
  * When the size is 0 (key window on, fewer than three whole rounds of query tiles, one
