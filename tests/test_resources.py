@@ -9,7 +9,7 @@ Budgets:
     waves w and w + 4 on one SIMD), so the compiler must report an occupancy of at least
     two waves per SIMD, i.e. at most 256 VGPRs + AGPRs per wave;
   * LDS per workgroup: BF16 four 16 KB K/V stages (64 KB), Sage three 16 KB K + V^T stages
-    plus the k_scale pairs and one code-path flag per wave (48 KB + 80 B); both far below the
+    plus the k_scale pairs, one code-path flag per wave and the tile's v_scale (48 KB + 592 B); both far below the
     160 KB of a CU.
 """
 import os
@@ -27,8 +27,8 @@ CSRC = os.path.join(ROOT, "image_dit_amd", "csrc")
 ATTENTION = {  # kernel name fragment -> max LDS bytes per workgroup
     "attn_fwd_bf16_kernel": 65536 + 64,
     "attn_fwd_bf16_split_kernel": 65536 + 64,
-    "sage_attn_fwd_kernel": 3 * (8192 + 8192) + 64 + 32,
-    "sage_attn_fwd_split_kernel": 3 * (8192 + 8192) + 64 + 32,
+    "sage_attn_fwd_kernel": 3 * (8192 + 8192) + 64 + 32 + 512,
+    "sage_attn_fwd_split_kernel": 3 * (8192 + 8192) + 64 + 32 + 512,
 }
 
 
